@@ -1,0 +1,245 @@
+"""fp64 CPU oracle for the forward pass of one token-chunked DiT transformer block.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports this module:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it. It shares no code with the HIP library.
+
+What it computes is the plain definition of the block that the pages chunk:
+
+* "LayerStream: H3 Chunking" (comfy.icu/node/LayerStreamH3Chunking), section
+  "How the slicing works": norms, modulation, the projections and the MLP are
+  token-wise and add into the residual stream; attention needs every key and
+  value for every query.
+* "Proposal: Generic memory-aware streaming execution for transformer models"
+  (github.com/Comfy-Org/ComfyUI/discussions/15920), sections "MLP planning" and
+  "Attention requires a stronger contract": a gated MLP followed by a linear
+  down projection, and attention over global K/V.
+
+Readings the pages leave open (each also listed in the design notes):
+LayerNorm without its own affine, biased variance, eps = 1e-6; DiT adaLN
+modulation ``norm * (1 + scale) + shift`` and a ``gate`` multiplying each
+branch before its residual add; no biases, no QK-norm, no positional transform,
+no mask; head h owns columns [h*dh, (h+1)*dh) of Q, K and V; scale 1/sqrt(dh);
+SwiGLU = silu(gate) * up with gate rows [0, F) and up rows [F, 2F) of ``w_gu``.
+
+Everything is fp64. A library matmul (numpy/OpenBLAS) serves as the matrix
+product step. Parity of every function here is pinned by the CPU tests
+(brute force, torch fp64 library routines, closed forms and invariants).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
+    "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
+]
+
+# The matrix-product step. Every product in this module goes through this one
+# name, so a test can substitute an order-stable product.
+matmul = np.matmul
+
+# Query rows per group when materialising scores: each query row's softmax is
+# independent of every other row, so rows are handled a group at a time only
+# to bound host memory.
+_SCORE_ELEMS = 1 << 25
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """Per token row: (x - mean) / sqrt(biased variance + eps); no affine.
+
+    The block's normalisation, applied per token ("How the slicing works";
+    "How it works", step 1, of the H3 MultiStream page). Two-pass statistics.
+    """
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(nrm: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """adaLN modulation of a normalised row: nrm * (1 + scale) + shift."""
+    return nrm * (1.0 + scale) + shift
+
+
+def linear(a: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """a [T, in] times w [out, in] transposed: y[t, o] = sum_i a[t, i] * w[o, i]."""
+    return matmul(a, w.T)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int) -> np.ndarray:
+    """Bidirectional multi-head softmax attention, exact two-pass softmax.
+
+    For each head h and query row i:
+        s_ij = <q_i^h, k_j^h> / sqrt(dh)         for every key j,
+        p_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij),
+        o_i^h = sum_j p_ij v_j^h.
+    Every query sees every key ("How the slicing works": attention is not
+    token-wise). ``q`` may hold any subset of query rows; ``k`` and ``v`` hold
+    all N keys.
+    """
+    t, d = q.shape
+    dh = d // n_heads
+    out = np.empty((t, d), dtype=np.float64)
+    rows = max(1, _SCORE_ELEMS // max(1, k.shape[0]))
+    inv = 1.0 / np.sqrt(dh)
+    for h in range(n_heads):
+        c = slice(h * dh, (h + 1) * dh)
+        kh_t = np.ascontiguousarray(k[:, c].T)
+        vh = np.ascontiguousarray(v[:, c])
+        for r0 in range(0, t, rows):
+            r1 = min(t, r0 + rows)
+            s = matmul(q[r0:r1, c], kh_t) * inv
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[r0:r1, c] = matmul(p, vh)
+    return out
+
+
+def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Weight-only int8: W[n, k] = s[n] * q[n, k], one scale per output row.
+
+    The TensorWiseINT8 layout of the Ascend port article (m.qwbw.cn/news/87515,
+    section 2.2) keeps one ``weight_scale`` per output row; slicing rows keeps
+    the projection exact ("How it works", step 3, of the H3 MultiStream page).
+    """
+    return np.asarray(s, np.float64)[:, None] * np.asarray(q, np.float64)
+
+
+def block_weights_f64(w: dict) -> dict:
+    """fp64 weight matrices from already-decoded arrays (dequantising int8 ones)."""
+    out = {}
+    for name in ("qkv", "o", "gu", "down"):
+        m = w["w_" + name]
+        if ("s_" + name) in w:
+            out[name] = dequantize_rows(m, w["s_" + name])
+        else:
+            out[name] = np.asarray(m, np.float64)
+    return out
+
+
+def _split(w: dict, d: int):
+    wqkv = w["qkv"]
+    return wqkv[:d], wqkv[d:2 * d], wqkv[2 * d:3 * d]
+
+
+def _mlp_delta(n2: np.ndarray, w: dict, ffn: int, f0: int = 0, f1: int | None = None) -> np.ndarray:
+    """W_down[:, f0:f1] (silu(W_gate[f0:f1] n2) * (W_up[f0:f1] n2)) for FFN features [f0, f1)."""
+    f1 = ffn if f1 is None else f1
+    g = linear(n2, w["gu"][f0:f1])
+    u = linear(n2, w["gu"][ffn + f0:ffn + f1])
+    return linear(silu(g) * u, w["down"][:, f0:f1])
+
+
+def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
+                  eps: float = 1e-6, want: tuple = ()) -> np.ndarray | tuple:
+    """Unchunked block forward; returns y [N, d] (and the named intermediates).
+
+    n1 = modulate(LN(x); shift1, scale1);  q, k, v = n1 W_{q,k,v}^T
+    o  = attention(q, k, v);               x1 = x + gate1 * (o W_o^T)
+    n2 = modulate(LN(x1); shift2, scale2); h = silu(n2 W_g^T) * (n2 W_u^T)
+    y  = x1 + gate2 * (h W_down^T)
+    ``want`` may name any of n1, q, k, v, o, x1, n2, h.
+    """
+    d = x.shape[1]
+    ffn = w["down"].shape[1]
+    sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
+    wq, wk, wv = _split(w, d)
+    n1 = modulate(layer_norm(x, eps), sh1, sc1)
+    q, k, v = linear(n1, wq), linear(n1, wk), linear(n1, wv)
+    o = attention(q, k, v, n_heads)
+    x1 = x + g1 * linear(o, w["o"])
+    n2 = modulate(layer_norm(x1, eps), sh2, sc2)
+    g = linear(n2, w["gu"][:ffn])
+    u = linear(n2, w["gu"][ffn:])
+    h = silu(g) * u
+    y = x1 + g2 * linear(h, w["down"])
+    if not want:
+        return y
+    loc = dict(n1=n1, q=q, k=k, v=v, o=o, x1=x1, n2=n2, h=h)
+    return (y,) + tuple(loc[name] for name in want)
+
+
+def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
+                          attn_chunk: int, mlp_chunk: int, ffn_chunk: int = 0,
+                          eps: float = 1e-6) -> np.ndarray:
+    """The pages' two-pass, token-chunked schedule of the same block, in place.
+
+    Follows "How the slicing works" (LayerStream: H3 Chunking) and "Attention
+    requires a stronger contract" (streaming proposal):
+      pass 1: for each slab of ``attn_chunk`` tokens, norm1 and project K and V
+              only, kept for the whole sequence;
+      pass 2: for each slice, recompute norm1 and Q, attend the slice against
+              the full K/V, out-project, and add the gated result into the
+              residual rows of that slice in place;
+      MLP:    for each slab of ``mlp_chunk`` tokens, norm2, SwiGLU and add the
+              gated result in place; with ``ffn_chunk`` > 0 the FFN features
+              are taken a slice at a time and the down-projected partials
+              accumulated ("MLP planning").
+    ``attn_chunk`` = 0 means one slice of all N tokens. The input is not
+    modified; the returned array is the residual stream after the block.
+    """
+    n, d = x.shape
+    ffn = w["down"].shape[1]
+    ca = n if attn_chunk <= 0 else min(attn_chunk, n)
+    cm = min(mlp_chunk, n)
+    fc = ffn if ffn_chunk <= 0 else min(ffn_chunk, ffn)
+    sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
+    wq, wk, wv = _split(w, d)
+    res = np.array(x, dtype=np.float64, copy=True)
+
+    k = np.empty((n, d))
+    v = np.empty((n, d))
+    for s0 in range(0, n, ca):                      # pass 1: K and V only
+        s1 = min(n, s0 + ca)
+        n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
+        k[s0:s1] = linear(n1, wk)
+        v[s0:s1] = linear(n1, wv)
+    for s0 in range(0, n, ca):                      # pass 2: Q slice vs global K/V
+        s1 = min(n, s0 + ca)
+        n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
+        o = attention(linear(n1, wq), k, v, n_heads)
+        res[s0:s1] += g1 * linear(o, w["o"])
+    for m0 in range(0, n, cm):                      # MLP, token slabs
+        m1 = min(n, m0 + cm)
+        n2 = modulate(layer_norm(res[m0:m1], eps), sh2, sc2)
+        acc = np.zeros((m1 - m0, d))
+        for f0 in range(0, ffn, fc):                # optional FFN feature slices
+            acc += _mlp_delta(n2, w, ffn, f0, min(ffn, f0 + fc))
+        res[m0:m1] += g2 * acc
+    return res
+
+
+def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.ndarray,
+               eps: float = 1e-6, want: tuple = ()) -> np.ndarray | tuple:
+    """The block output for the query rows ``rows`` only (exact for those rows).
+
+    norm1 and K/V are computed for all N tokens, because every query attends
+    every key; every later step is per token, so it runs on the chosen rows.
+    """
+    d = x.shape[1]
+    ffn = w["down"].shape[1]
+    sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
+    wq, wk, wv = _split(w, d)
+    n1_all = modulate(layer_norm(x, eps), sh1, sc1)
+    k, v = linear(n1_all, wk), linear(n1_all, wv)
+    del n1_all
+    xr = x[rows]
+    n1 = modulate(layer_norm(xr, eps), sh1, sc1)
+    q = linear(n1, wq)
+    o = attention(q, k, v, n_heads)
+    x1 = xr + g1 * linear(o, w["o"])
+    n2 = modulate(layer_norm(x1, eps), sh2, sc2)
+    g = linear(n2, w["gu"][:ffn])
+    u = linear(n2, w["gu"][ffn:])
+    h = silu(g) * u
+    y = x1 + g2 * linear(h, w["down"])
+    if not want:
+        return y
+    loc = dict(n1=n1, q=q, k=k[rows], v=v[rows], o=o, x1=x1, n2=n2, h=h)
+    return (y,) + tuple(loc[name] for name in want)
