@@ -1,0 +1,200 @@
+"""Benchmark of one token-chunked DiT block forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config large] [--no-cpu-baseline]
+
+A step is one full block forward (pass 1 K/V, pass 2 Q/attention/out-proj,
+SwiGLU MLP) over the whole token sequence, preceded by a device copy that
+restores the input x (the forward overwrites x in place). Inputs are seeded
+synthetic arrays already resident in HBM when timing starts. Prints one JSON
+line. The dominant kernel (attention) is timed per launch with HIP events on
+the stream the library launches on, over a second pass of K steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT-block tokens/s & % bf16 MFMA peak at 32k tokens; peak workspace bytes"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(shape, inputs, rows: int) -> dict:
+    """The fp64 oracle on a bounded sample: norm1 and K/V for all N tokens plus
+    the remaining steps for ``rows`` sampled query rows; extrapolated to N rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.dit_block as O
+    from memory_bounded_chunked_amd import synth
+
+    x = synth.to_f64(inputs["x"])
+    mod = inputs["mod"].astype(np.float64)
+    w = O.block_weights_f64({k: synth.to_f64(v) for k, v in inputs.items() if k[:2] in ("w_", "s_")})
+    d = shape.d
+    sh1, sc1 = mod[0], mod[1]
+    t0 = time.perf_counter()
+    n1 = O.modulate(O.layer_norm(x, shape.eps), sh1, sc1)
+    k = O.linear(n1, w["qkv"][d:2 * d])
+    v = O.linear(n1, w["qkv"][2 * d:])
+    del n1
+    t_kv = time.perf_counter() - t0
+    sel = synth.sample_rows(shape.n_tokens, rows, seed=1)
+    t1 = time.perf_counter()
+    xr = x[sel]
+    n1r = O.modulate(O.layer_norm(xr, shape.eps), sh1, sc1)
+    o = O.attention(O.linear(n1r, w["qkv"][:d]), k, v, shape.n_heads)
+    x1 = xr + mod[2] * O.linear(o, w["o"])
+    n2 = O.modulate(O.layer_norm(x1, shape.eps), mod[3], mod[4])
+    f = shape.ffn
+    h = O.silu(O.linear(n2, w["gu"][:f])) * O.linear(n2, w["gu"][f:])
+    _ = x1 + mod[5] * O.linear(h, w["down"])
+    t_rows = time.perf_counter() - t1
+    t_full = t_kv + t_rows * shape.n_tokens / len(sel)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": shape.n_tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 oracle: norm1+K/V for all {shape.n_tokens} tokens ({t_kv:.1f} s) + steps for "
+                       f"{len(sel)} sampled query rows ({t_rows:.1f} s); full block extrapolated "
+                       f"to {t_full:.0f} s"),
+            "measured_s": round(t_kv + t_rows, 2), "cpu_count": os.cpu_count()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="large")
+    ap.add_argument("--attn-chunk", type=int, default=None)
+    ap.add_argument("--mlp-chunk", type=int, default=None)
+    ap.add_argument("--ffn-chunk", type=int, default=None)
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the block path is "
+              "single-GPU: no collectives)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from memory_bounded_chunked_amd import block as B
+    from memory_bounded_chunked_amd import synth
+
+    shape = synth.CONFIGS[args.config]
+    ca = shape.attn_chunk if args.attn_chunk is None else args.attn_chunk
+    cm = shape.mlp_chunk if args.mlp_chunk is None else args.mlp_chunk
+    fc = shape.ffn_chunk if args.ffn_chunk is None else args.ffn_chunk
+    dev = "cuda:0"
+    t0 = time.perf_counter()
+    inputs = synth.make_inputs(shape, seed=0)
+    log(f"[bench] inputs for {shape.name} drawn in {time.perf_counter() - t0:.1f}s")
+    blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
+    x = x0.clone()
+    ws_bytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        x.copy_(x0)
+        blk.forward(x, mod, ca, cm, fc, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.3f}s)")
+
+    # per-kernel HIP-event timing over a second pass of the same steps
+    B.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = B.profile_read()
+    B.profile_enable(False)
+    kernels = {k: {"total_ms_per_step": round(t / args.steps, 4), "launches_per_step": n // args.steps,
+                   "avg_launch_ms": round(t / n, 4) if n else None} for k, (t, n) in prof.items()}
+    log("[bench] per-kernel: " + json.dumps(kernels))
+
+    n, d = shape.n_tokens, shape.d
+    flops = shape.flops
+    tflops = flops / (ms / 1e3) / 1e12
+    peak = PEAK_F32_TFLOPS if shape.dtype == "f32" else PEAK_BF16_TFLOPS
+    att_t, att_n = prof["attention"]
+    ca_eff = n if ca == 0 else min(ca, n)
+    # algorithmic FLOPs per attention launch: 4*d per (query, key) pair x (slice rows x N keys);
+    # every launch in this schedule has ca_eff rows unless N % ca_eff leaves a shorter last slice
+    pairs = n * n  # all launches together cover N queries x N keys
+    att_tflops = 4.0 * d * pairs / (att_t / 1e3) / 1e12 if att_t > 0 else None
+    roofline = {
+        "kernel": "attention",
+        "bound": "mfma",
+        "achieved": round(att_tflops, 1) if att_tflops else None,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(att_tflops / peak, 4) if att_tflops else None,
+        "traffic": None,
+        "avg_launch_ms": round(att_t / att_n, 4) if att_n else None,
+        "flops_per_launch": 4.0 * d * ca_eff * n,
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(n / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "w8_bf16": "w8a16-bf16"}[shape.dtype],
+        "data": "synthetic (seeded PCG64 inputs; see DESIGN.md recipe)",
+        "config": {
+            "workload": (f"{shape.name} DiT block forward: d={d}, {shape.n_heads}x{shape.head_dim} heads, "
+                         f"SwiGLU F={shape.ffn}, N={n} tokens, batch 1"),
+            "n_tokens": n, "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
+            "peak_workspace_bytes": ws_bytes,
+            "tflops": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / peak, 4),
+            "flops_per_step": flops,
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    blk.close()
+    del x, x0, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: fp64 oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_rows)
+        log(f"[bench] cpu_baseline done: {result['cpu_baseline']['sample']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

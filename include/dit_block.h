@@ -1,0 +1,142 @@
+/*
+ * dit_block.h - C ABI of the token-chunked, activation-bounded forward pass of
+ * one DiT transformer block on MI355X (gfx950).
+ *
+ * The method is the one of "LayerStream: H3 Chunking"
+ * (comfy.icu/node/LayerStreamH3Chunking), sections "How the slicing works" and
+ * "The two numbers you set", and of "Proposal: Generic memory-aware streaming
+ * execution for transformer models" (github.com/Comfy-Org/ComfyUI/discussions/
+ * 15920), sections "MLP planning" and "Attention requires a stronger
+ * contract":
+ *   - norms, modulation, projections and the MLP are token-wise and run on
+ *     token slices that add into the residual stream in place;
+ *   - attention runs in two passes: pass 1 keeps only K and V for all tokens;
+ *     pass 2 recomputes Q per slice, attends the slice against the full K/V,
+ *     out-projects and adds into the residual;
+ *   - the gated MLP can additionally be split along its FFN features, each
+ *     slice projected, activated, down-projected and accumulated.
+ *
+ * The block computed (fp64 meaning; the oracle is this definition):
+ *   n1 = LN(x) * (1 + scale1) + shift1          LN: no affine, biased var, eps
+ *   q, k, v = n1 Wq^T, n1 Wk^T, n1 Wv^T          Wq|Wk|Wv = rows of w_qkv
+ *   o  = softmax(q k^T / sqrt(dh)) v             per head, bidirectional, no mask
+ *   x1 = x + gate1 * (o Wo^T)
+ *   n2 = LN(x1) * (1 + scale2) + shift2
+ *   y  = x1 + gate2 * ((silu(n2 Wg^T) * (n2 Wu^T)) Wd^T)   Wg|Wu = rows of w_gu
+ *
+ * All functions are thread-safe for distinct handles. A handle may be used by
+ * one stream at a time. No function allocates device memory; dit_block_forward
+ * only enqueues kernels on the given stream and never synchronises.
+ */
+#ifndef DIT_BLOCK_H
+#define DIT_BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. Every argument error is reported before any kernel is
+ * enqueued; nothing falls back to another path (the streaming proposal's
+ * "Patch compatibility" section: fail closed rather than degrade). */
+#define DIT_OK 0
+#define DIT_EINVAL (-1)  /* bad argument: null pointer, shape, chunk value, alignment */
+#define DIT_ENOSPC (-2)  /* workspace_bytes below dit_block_peak_workspace() */
+#define DIT_EHIP (-3)    /* the HIP runtime reported a launch error */
+
+/* Storage types. F32: activations and weights fp32, fp32 arithmetic.
+ * BF16: activations and weights bf16, fp32 accumulation and softmax.
+ * W8_BF16: bf16 activations, int8 weights with one fp32 scale per output row
+ * (W[n][k] = s[n] * q[n][k]; the per-row weight_scale of the Ascend port's
+ * TensorWiseINT8 layout, m.qwbw.cn/news/87515, section 2.2). */
+#define DIT_F32 0
+#define DIT_BF16 1
+#define DIT_W8_BF16 2
+
+typedef struct dit_block dit_block;
+
+typedef struct dit_block_desc {
+  int64_t d;         /* hidden size; must equal n_heads * head_dim */
+  int64_t n_heads;
+  int64_t head_dim;  /* 64 or 128 */
+  int64_t ffn;       /* SwiGLU width F; multiple of 64 */
+  int32_t dtype;     /* DIT_F32, DIT_BF16 or DIT_W8_BF16 */
+  float eps;         /* LayerNorm epsilon (1e-6 for the DiT blocks here) */
+} dit_block_desc;
+
+/* Device pointers, row-major [out][in], borrowed: the caller keeps them alive
+ * and unchanged until dit_block_destroy. Element type: fp32 (F32), bf16
+ * (BF16) or int8 (W8_BF16). 16-byte aligned. */
+typedef struct dit_block_weights {
+  const void* w_qkv;   /* [3d][d]: rows [0,d) = Wq, [d,2d) = Wk, [2d,3d) = Wv;
+                          head h owns rows h*dh .. h*dh+dh-1 of each */
+  const void* w_o;     /* [d][d] */
+  const void* w_gu;    /* [2F][d]: rows [0,F) = gate, [F,2F) = up; feature f
+                          pairs gate row f with up row F+f */
+  const void* w_down;  /* [d][F] */
+  const float* s_qkv;  /* W8_BF16 only: fp32 scale per output row, [3d] */
+  const float* s_o;    /* [d] */
+  const float* s_gu;   /* [2F] */
+  const float* s_down; /* [d] */
+} dit_block_weights;
+
+/* Validate the descriptor and weight pointers and create a handle that holds
+ * only host metadata (no device calls). *out is set on success.
+ * Errors: DIT_EINVAL for a null pointer, d != n_heads*head_dim, head_dim not
+ * in {64,128}, ffn < 64 or not a multiple of 64, an unknown dtype, eps <= 0,
+ * a weight pointer not 16-byte aligned, or a missing W8 scale. */
+int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit_block** out);
+
+/* Exact workspace bytes that dit_block_forward needs for these arguments
+ * (host arithmetic only). With e = activation bytes (4 for F32, else 2),
+ * Ca = attn_chunk_tokens (0 -> N), Cm = mlp_chunk_tokens, fc =
+ * ffn_chunk_features (0 -> F), each clamped to N (fc to F), S = max(Ca, Cm)
+ * and Np = N rounded up to 64, each region rounded up to 256 bytes:
+ *     N*d*e           global K            (kept for the whole sequence)
+ *   + d*Np*e          global V, stored transposed [d][Np]
+ *   + S*d*4           fp32 residual staging for one super-slice
+ *   + max(2*Ca*d*e, Cm*d*e + Cm*fc*e)    slabs: norm/O + Q, or norm2 + h
+ * Only the K/V terms grow with N ("Where people get burned": K and V for the
+ * whole sequence stay resident and set the memory floor). Same argument
+ * rules and errors as dit_block_forward. */
+int dit_block_peak_workspace(const dit_block* h, int64_t n_tokens, int64_t attn_chunk_tokens,
+                             int64_t mlp_chunk_tokens, int64_t ffn_chunk_features,
+                             size_t* bytes_out);
+
+/* One block forward, in place.
+ *   x          [N][d] activations (fp32 for F32, else bf16), read and
+ *              overwritten with the block output y. 16-byte aligned.
+ *   mod        [6][d] fp32: shift1, scale1, gate1, shift2, scale2, gate2.
+ *   n_tokens   N >= 1.
+ *   attn_chunk_tokens   query tokens per attention slice (>= 0; 0 = one slice
+ *              of all N tokens, the pages' "stock attention" setting).
+ *   mlp_chunk_tokens    tokens per MLP slice (>= 1).
+ *   ffn_chunk_features  FFN features per MLP slice (0 = all F; otherwise a
+ *              multiple of 64; the last slice may be shorter).
+ *   Chunk values above N (F) are clamped. Output bytes are identical for every
+ *   (attn_chunk_tokens, mlp_chunk_tokens) at a fixed ffn_chunk_features.
+ *   workspace  device scratch of at least dit_block_peak_workspace() bytes,
+ *              16-byte aligned, owned by the caller; contents undefined after.
+ *   stream     a hipStream_t (NULL = the null stream).
+ * Enqueues and returns; no allocation, no host synchronisation.
+ * Errors: DIT_EINVAL (null pointer, N < 1, negative chunk, mlp_chunk_tokens <
+ * 1, ffn_chunk_features not a multiple of 64, misaligned pointer),
+ * DIT_ENOSPC, DIT_EHIP. On an error return nothing has been enqueued, except
+ * for DIT_EHIP, which reports a failed launch. */
+int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
+                      int64_t attn_chunk_tokens, int64_t mlp_chunk_tokens,
+                      int64_t ffn_chunk_features, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Release the handle (host memory only; the weights stay the caller's). */
+void dit_block_destroy(dit_block* h);
+
+/* Static message for a return code. */
+const char* dit_block_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_BLOCK_H */

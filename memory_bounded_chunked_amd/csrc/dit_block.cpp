@@ -1,0 +1,408 @@
+// C ABI of the block: argument validation, the closed-form workspace, the
+// workspace carve and the two-pass, token-chunked schedule.
+//
+// Schedule ("LayerStream: H3 Chunking", sections "How the slicing works" and
+// "The two numbers you set"; streaming proposal, "Attention requires a
+// stronger contract" and "MLP planning"):
+//   pass 1   for each slab of Ca tokens: norm1 -> K rows and V^T columns of the
+//            global K/V (only the K and V weight rows are multiplied);
+//   pass 2   for each super-slice of S = max(Ca, Cm) tokens:
+//              for each Ca-slab: norm1 -> Q -> attention vs global K/V -> O
+//                                -> stage = x + gate1 * (O Wo^T)        (fp32)
+//              for each Cm-slab: norm2(stage) -> SwiGLU (per FFN feature slice)
+//                                -> x = stage + gate2 * (h Wd^T)        (in place)
+// Pass 1 ends before anything writes x; afterwards each super-slice reads and
+// writes only its own rows of x. The residual after attention stays in fp32
+// in `stage` and the block output is rounded once, when it is written to x.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/dit_block.h"
+#include "../../include/dit_block_profile.h"
+#include "../../include/dit_block_steps.h"
+#include "kernels.hpp"
+
+struct dit_block {
+  dit_block_desc desc;
+  dit_block_weights w;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t act_bytes(int dtype) { return dtype == DIT_F32 ? 4 : 2; }
+
+struct Plan {
+  int64_t n, ca, cm, fc, s, np;
+  size_t off_k, off_vt, off_stage, off_slab, slab_b, total;
+};
+
+int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chunk, int64_t ffn_chunk,
+              Plan* p) {
+  if (!h || !p) return DIT_EINVAL;
+  if (n < 1 || attn_chunk < 0 || mlp_chunk < 1 || ffn_chunk < 0 || ffn_chunk % 64) return DIT_EINVAL;
+  const int64_t d = h->desc.d, f = h->desc.ffn, e = act_bytes(h->desc.dtype);
+  p->n = n;
+  p->ca = attn_chunk == 0 ? n : std::min(attn_chunk, n);
+  p->cm = std::min(mlp_chunk, n);
+  p->fc = ffn_chunk == 0 ? f : std::min(ffn_chunk, f);
+  p->s = std::max(p->ca, p->cm);
+  p->np = (n + 63) / 64 * 64;
+  const size_t k_bytes = round_up((size_t)n * d * e, kAlign);
+  const size_t vt_bytes = round_up((size_t)d * p->np * e, kAlign);
+  const size_t stage_bytes = round_up((size_t)p->s * d * 4, kAlign);
+  const size_t attn_a = round_up((size_t)p->ca * d * e, kAlign);
+  const size_t mlp_a = round_up((size_t)p->cm * d * e, kAlign);
+  const size_t mlp_h = round_up((size_t)p->cm * p->fc * e, kAlign);
+  p->off_k = 0;
+  p->off_vt = k_bytes;
+  p->off_stage = p->off_vt + vt_bytes;
+  p->off_slab = p->off_stage + stage_bytes;
+  p->slab_b = attn_a;  // offset of the Q slab within the slab region
+  p->total = p->off_slab + std::max(2 * attn_a, mlp_a + mlp_h);
+  return DIT_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_EHIP; }
+
+// Optional per-kernel event timing (dit_block_profile.h).
+struct Profiler {
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<Rec> recs;
+
+  hipEvent_t take() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Profiler g_prof;
+
+// Runs one launch, bracketed by events when profiling is on.
+template <typename F>
+hipError_t run_step(int kind, hipStream_t st, F&& launch) {
+  if (!g_prof.on) return launch();
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  hipEvent_t a = g_prof.take(), b = g_prof.take();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  if (e == hipSuccess) g_prof.recs.push_back({kind, a, b});
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_block_strerror(int code) {
+  switch (code) {
+    case DIT_OK: return "ok";
+    case DIT_EINVAL: return "invalid argument";
+    case DIT_ENOSPC: return "workspace too small";
+    case DIT_EHIP: return "HIP launch error";
+    default: return "unknown error";
+  }
+}
+
+int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit_block** out) {
+  if (!desc || !w || !out) return DIT_EINVAL;
+  const dit_block_desc& d = *desc;
+  if (d.dtype != DIT_F32 && d.dtype != DIT_BF16 && d.dtype != DIT_W8_BF16) return DIT_EINVAL;
+  if (d.head_dim != 64 && d.head_dim != 128) return DIT_EINVAL;
+  if (d.n_heads < 1 || d.d != d.n_heads * d.head_dim || d.d > 8192) return DIT_EINVAL;
+  if (d.ffn < 64 || d.ffn % 64) return DIT_EINVAL;
+  if (!(d.eps > 0.f)) return DIT_EINVAL;
+  const void* ptrs[4] = {w->w_qkv, w->w_o, w->w_gu, w->w_down};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return DIT_EINVAL;
+  if (d.dtype == DIT_W8_BF16) {
+    if (!w->s_qkv || !w->s_o || !w->s_gu || !w->s_down) return DIT_EINVAL;
+  }
+  dit_block* h = new (std::nothrow) dit_block;
+  if (!h) return DIT_EINVAL;
+  h->desc = d;
+  h->w = *w;
+  *out = h;
+  return DIT_OK;
+}
+
+void dit_block_destroy(dit_block* h) { delete h; }
+
+int dit_block_peak_workspace(const dit_block* h, int64_t n_tokens, int64_t attn_chunk_tokens,
+                             int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, size_t* bytes_out) {
+  if (!bytes_out) return DIT_EINVAL;
+  Plan p;
+  const int rc = make_plan(h, n_tokens, attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features, &p);
+  if (rc != DIT_OK) return rc;
+  *bytes_out = p.total;
+  return DIT_OK;
+}
+
+int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens, int64_t attn_chunk_tokens,
+                      int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  Plan p;
+  const int rc = make_plan(h, n_tokens, attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features, &p);
+  if (rc != DIT_OK) return rc;
+  if (!x || !mod || !workspace) return DIT_EINVAL;
+  if (!aligned16(x) || !aligned16(mod) || !aligned16(workspace)) return DIT_EINVAL;
+  if (workspace_bytes < p.total) return DIT_ENOSPC;
+
+  using namespace dit;
+  const dit_block_desc& dsc = h->desc;
+  const int dt = dsc.dtype;
+  const int f32 = dt == DIT_F32;
+  const int64_t d = dsc.d, ffn = dsc.ffn, e = act_bytes(dt), n = p.n;
+  const bool w8 = dt == DIT_W8_BF16;
+  const int64_t wb = w8 ? 1 : e;  // bytes per weight element
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  char* ws = static_cast<char*>(workspace);
+  char* kbuf = ws + p.off_k;
+  char* vtbuf = ws + p.off_vt;
+  float* stage = reinterpret_cast<float*>(ws + p.off_stage);
+  char* slab_a = ws + p.off_slab;
+  char* slab_b = ws + p.off_slab + p.slab_b;
+  char* xb = static_cast<char*>(x);
+
+  const float *sh1 = mod, *sc1 = mod + d, *g1 = mod + 2 * d;
+  const float *sh2 = mod + 3 * d, *sc2 = mod + 4 * d, *g2 = mod + 5 * d;
+  const char* wqkv = static_cast<const char*>(h->w.w_qkv);
+  const float* s_qkv = w8 ? h->w.s_qkv : nullptr;
+
+  hipError_t err = hipSuccess;
+#define DIT_TRY(kind, call)                                  \
+  do {                                                       \
+    err = run_step((kind), st, [&]() { return (call); });    \
+    if (err != hipSuccess) return DIT_EHIP;                  \
+  } while (0)
+
+  // ---- pass 1: K and V for all tokens, in slabs of Ca tokens
+  for (int64_t s0 = 0; s0 < n; s0 += p.ca) {
+    const int64_t c = std::min(p.ca, n - s0);
+    DIT_TRY(DIT_K_MODNORM, launch_modnorm(f32, f32, xb + s0 * d * e, d, sh1, sc1, slab_a, d, c, (int)d, dsc.eps, st));
+    GemmArgs g{};
+    g.a = slab_a;
+    g.lda = d;
+    g.M = c;
+    g.N = d;
+    g.K = d;
+    g.ldb = d;
+    g.b = wqkv + d * d * wb;
+    g.bscale = s_qkv ? s_qkv + d : nullptr;
+    g.out = kbuf + s0 * d * e;
+    g.ldo = d;
+    DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE, g, st));
+    g.b = wqkv + 2 * d * d * wb;
+    g.bscale = s_qkv ? s_qkv + 2 * d : nullptr;
+    g.out = vtbuf + s0 * e;
+    g.ldo = p.np;
+    DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
+  }
+
+  // ---- pass 2: super-slices of S tokens
+  for (int64_t t0 = 0; t0 < n; t0 += p.s) {
+    const int64_t tn = std::min(p.s, n - t0);
+    for (int64_t s0 = t0; s0 < t0 + tn; s0 += p.ca) {
+      const int64_t c = std::min(p.ca, t0 + tn - s0);
+      DIT_TRY(DIT_K_MODNORM, launch_modnorm(f32, f32, xb + s0 * d * e, d, sh1, sc1, slab_a, d, c, (int)d, dsc.eps, st));
+      GemmArgs g{};
+      g.a = slab_a;
+      g.lda = d;
+      g.M = c;
+      g.N = d;
+      g.K = d;
+      g.b = wqkv;
+      g.ldb = d;
+      g.bscale = s_qkv;
+      g.out = slab_b;
+      g.ldo = d;
+      DIT_TRY(DIT_K_Q_PROJ, launch_gemm(dt, EPI_STORE, g, st));
+      DIT_TRY(DIT_K_ATTENTION, launch_attention(dt, slab_b, d, kbuf, d, vtbuf, p.np, slab_a, d, c, n, (int)dsc.n_heads,
+                               (int)dsc.head_dim, st));
+      GemmArgs o{};
+      o.a = slab_a;
+      o.lda = d;
+      o.M = c;
+      o.N = d;
+      o.K = d;
+      o.b = h->w.w_o;
+      o.ldb = d;
+      o.bscale = w8 ? h->w.s_o : nullptr;
+      o.out = stage + (s0 - t0) * d;
+      o.ldo = d;
+      o.aux = xb + s0 * d * e;
+      o.ldaux = d;
+      o.gate = g1;
+      DIT_TRY(DIT_K_OUT_PROJ, launch_gemm(dt, EPI_RESID, o, st));
+    }
+    for (int64_t m0 = t0; m0 < t0 + tn; m0 += p.cm) {
+      const int64_t c = std::min(p.cm, t0 + tn - m0);
+      float* srows = stage + (m0 - t0) * d;
+      char* n2 = slab_a;
+      char* hbuf = slab_a + round_up((size_t)p.cm * d * e, kAlign);
+      DIT_TRY(DIT_K_MODNORM, launch_modnorm(1, f32, srows, d, sh2, sc2, n2, d, c, (int)d, dsc.eps, st));
+      for (int64_t f0 = 0; f0 < ffn; f0 += p.fc) {
+        const int64_t fl = std::min(p.fc, ffn - f0);
+        GemmArgs gu{};
+        gu.a = n2;
+        gu.lda = d;
+        gu.M = c;
+        gu.N = fl;
+        gu.K = d;
+        gu.b = static_cast<const char*>(h->w.w_gu) + f0 * d * wb;
+        gu.ldb = d;
+        gu.up_offset = ffn;
+        gu.bscale = w8 ? h->w.s_gu + f0 : nullptr;
+        gu.out = hbuf;
+        gu.ldo = p.fc;
+        DIT_TRY(DIT_K_GATE_UP, launch_gemm(dt, EPI_GATEUP, gu, st));
+        const bool last = f0 + fl >= ffn;
+        GemmArgs dn{};
+        dn.a = hbuf;
+        dn.lda = p.fc;
+        dn.M = c;
+        dn.N = d;
+        dn.K = fl;
+        dn.b = static_cast<const char*>(h->w.w_down) + f0 * wb;
+        dn.ldb = ffn;
+        dn.bscale = w8 ? h->w.s_down : nullptr;
+        dn.gate = g2;
+        if (last) {
+          dn.out = xb + m0 * d * e;
+          dn.ldo = d;
+          dn.aux = srows;
+          dn.ldaux = d;
+          DIT_TRY(DIT_K_DOWN, launch_gemm(dt, EPI_FINAL, dn, st));
+        } else {
+          dn.out = srows;
+          dn.ldo = d;
+          DIT_TRY(DIT_K_DOWN, launch_gemm(dt, EPI_ACCUM, dn, st));
+        }
+      }
+    }
+  }
+#undef DIT_TRY
+  (void)err;
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------- profiling
+
+int dit_profile_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (on) {
+    g_prof.recs.clear();
+    g_prof.used = 0;
+  }
+  g_prof.on = on != 0;
+  return DIT_OK;
+}
+
+int dit_profile_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= DIT_K_COUNT || !total_ms || !launches) return DIT_EINVAL;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  double t = 0.0;
+  int64_t n = 0;
+  for (const auto& r : g_prof.recs) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return DIT_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return DIT_EHIP;
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *launches = n;
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------- step-level entry points
+
+int dit_modnorm(int32_t in_dtype, int32_t out_dtype, const void* x, int64_t ldx, const float* shift,
+                const float* scale, void* out, int64_t ldo, int64_t rows, int64_t d, float eps, void* stream) {
+  if ((in_dtype != DIT_F32 && in_dtype != DIT_BF16) || (out_dtype != DIT_F32 && out_dtype != DIT_BF16))
+    return DIT_EINVAL;
+  if (!x || !shift || !scale || !out || rows < 0 || d < 8 || d > 8192 || d % 8) return DIT_EINVAL;
+  if (ldx < d || ldo < d || ldx % 8 || ldo % 8 || !(eps > 0.f)) return DIT_EINVAL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(shift) || !aligned16(scale)) return DIT_EINVAL;
+  if (rows == 0) return DIT_OK;
+  return hip_status(dit::launch_modnorm(in_dtype == DIT_F32, out_dtype == DIT_F32, x, ldx, shift, scale, out,
+                                        ldo, rows, (int)d, eps, static_cast<hipStream_t>(stream)));
+}
+
+int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
+                  int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int64_t n_heads,
+                  int64_t head_dim, void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EINVAL;
+  if (!q || !k || !vt || !o || n_q < 0 || n_kv < 1 || n_heads < 1) return DIT_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return DIT_EINVAL;
+  const int64_t d = n_heads * head_dim;
+  if (ldq < d || ldk < d || ldo < d || ldvt < n_kv) return DIT_EINVAL;
+  if (ldq % 8 || ldk % 8 || ldo % 8 || ldvt % 8) return DIT_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return DIT_EINVAL;
+  if (n_q == 0) return DIT_OK;
+  return hip_status(dit::launch_attention(dtype, q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, (int)n_heads,
+                                          (int)head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int dit_linear(int32_t dtype, int32_t epilogue, const void* a, int64_t lda, const void* w, int64_t ldw,
+               const float* w_scale, int64_t up_offset, int64_t m, int64_t n, int64_t k, void* out,
+               int64_t ldo, const void* aux, int64_t ldaux, const float* gate, void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16 && dtype != DIT_W8_BF16) return DIT_EINVAL;
+  if (epilogue < DIT_EPI_STORE || epilogue > DIT_EPI_FINAL) return DIT_EINVAL;
+  if (!a || !w || !out || m < 0 || n < 64 || n % 64 || k < 1) return DIT_EINVAL;
+  if (k % (dtype == DIT_F32 ? 32 : 64)) return DIT_EINVAL;
+  if (lda < k || ldw < k || lda % 8 || ldo % 8 || ldw % (dtype == DIT_W8_BF16 ? 16 : 8)) return DIT_EINVAL;
+  if ((dtype == DIT_W8_BF16) != (w_scale != nullptr)) return DIT_EINVAL;
+  const bool needs_aux = epilogue == DIT_EPI_RESID || epilogue == DIT_EPI_FINAL;
+  const bool needs_gate = needs_aux || epilogue == DIT_EPI_ACCUM;
+  if (needs_aux && (!aux || ldaux < n || ldaux % 8)) return DIT_EINVAL;
+  if (needs_gate && !gate) return DIT_EINVAL;
+  if (epilogue == DIT_EPI_GATEUP && up_offset < n) return DIT_EINVAL;
+  if (epilogue == DIT_EPI_STORE_T ? ldo < m : ldo < n) return DIT_EINVAL;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out) || (aux && !aligned16(aux))) return DIT_EINVAL;
+  if (m == 0) return DIT_OK;
+  dit::GemmArgs g{};
+  g.a = a;
+  g.lda = lda;
+  g.b = w;
+  g.ldb = ldw;
+  g.bscale = w_scale;
+  g.up_offset = up_offset;
+  g.M = m;
+  g.N = n;
+  g.K = k;
+  g.out = out;
+  g.ldo = ldo;
+  g.aux = aux;
+  g.ldaux = ldaux;
+  g.gate = gate;
+  return hip_status(dit::launch_gemm(dtype, static_cast<dit::Epilogue>(epilogue), g,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

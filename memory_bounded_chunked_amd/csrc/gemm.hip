@@ -1,0 +1,326 @@
+// K2: C[M][N] = A[M][K] * B[N][K]^T on MFMA, with fused epilogues.
+//
+// A holds token rows (activations), B holds weight rows [out][in]; both are
+// K-contiguous, which is the operand layout MFMA consumes directly. Tiles of
+// A and B are staged through LDS (double buffered: the next k-tile's global
+// loads are in flight while the current one is multiplied). LDS rows are
+// 128 B (8 chunks of 16 B) and chunk c of row r lives at slot c ^ (r & 7), so
+// the 8 lanes served together by a 16-byte LDS read always hit distinct banks.
+//
+// Each output element is the same fixed sequence: 32x32x16 bf16 MFMA (or
+// 32x32x2 fp32 MFMA for the F32 block) accumulations over k in increasing
+// k-tile order, followed by the epilogue. That sequence does not depend on
+// M, on the tile's position or on which token slab is being projected, so a
+// row's result is bit-identical however the tokens are sliced ("How the
+// slicing works": the projections and the MLP are token-wise).
+//
+// Weight-only int8 (W8_BF16): B is int8 in HBM and is widened exactly to bf16
+// on its way into LDS (|q| <= 127 needs 7 significant bits); the per-row scale
+// multiplies the fp32 accumulator in the epilogue.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dit {
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// 16 int8 -> 16 bf16 (exact).
+__device__ __forceinline__ void i8x16_to_bf16(const u32x4& q, u32x4& lo, u32x4& hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = q[j];
+    const float f0 = (float)(int8_t)(v & 0xff);
+    const float f1 = (float)(int8_t)((v >> 8) & 0xff);
+    const float f2 = (float)(int8_t)((v >> 16) & 0xff);
+    const float f3 = (float)(int8_t)(v >> 24);
+    // exact: every |q| <= 127 is representable in bf16, so truncation is exact
+    w[2 * j] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    w[2 * j + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  }
+  lo = u32x4{w[0], w[1], w[2], w[3]};
+  hi = u32x4{w[4], w[5], w[6], w[7]};
+}
+
+template <typename T>
+__device__ __forceinline__ float load_act(const T* p) {
+  if constexpr (sizeof(T) == 2)
+    return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  else
+    return *p;
+}
+template <typename T>
+__device__ __forceinline__ void store_act(T* p, float v) {
+  if constexpr (sizeof(T) == 2)
+    *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(v);
+  else
+    *p = v;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+template <typename TA, typename TB, int EPI, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
+  constexpr int NTHR = WM * WN * 64;
+  constexpr bool A_F32 = sizeof(TA) == 4;
+  constexpr bool B_I8 = sizeof(TB) == 1;
+  constexpr int BK = A_F32 ? 32 : 64;  // k elements per tile: 128 B of an A row
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MT = WTM / 32, NTL = WTN / 32;
+  constexpr int A_LD = BM * 8 / NTHR;
+  constexpr int B_GROW = B_I8 ? 4 : 8;  // 16-B global chunks per B tile row
+  constexpr int B_LD = BN * B_GROW / NTHR;
+  constexpr int STAGE = (BM + BN) * 128;
+  static_assert(BM * 8 % NTHR == 0 && BN * B_GROW % NTHR == 0, "tile/threads");
+  static_assert(EPI != EPI_GATEUP || NTL % 2 == 0, "gate/up tiles come in pairs");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
+  const int64_t tiles_n = g.N / OUT_BN;
+  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = tm * BM;
+
+  const char* A = static_cast<const char*>(g.a);
+  const char* B = static_cast<const char*>(g.b);
+
+  // Global source of B tile row r.
+  auto b_row = [&](int r) -> int64_t {
+    if constexpr (EPI == EPI_GATEUP) {
+      const int grp = r >> 5;
+      const int64_t feat = tn * (BN / 2) + (grp >> 1) * 32 + (r & 31);
+      return feat + ((grp & 1) ? g.up_offset : 0);
+    } else {
+      return tn * BN + r;
+    }
+  };
+
+  u32x4 ra[A_LD], rb[B_LD];
+  auto load_tiles = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int c = tid + i * NTHR;
+      const int r = c >> 3, ch = c & 7;
+      const int64_t gr = m0 + r;
+      if (gr < g.M)
+        ra[i] = *reinterpret_cast<const u32x4*>(A + (gr * g.lda + k0) * (int64_t)sizeof(TA) + ch * 16);
+      else
+        ra[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int c = tid + i * NTHR;
+      const int r = c / B_GROW, ch = c % B_GROW;
+      rb[i] = *reinterpret_cast<const u32x4*>(B + (b_row(r) * g.ldb + k0) * (int64_t)sizeof(TB) + ch * 16);
+    }
+  };
+  auto store_tiles = [&](int buf) {
+    char* As = smem + buf * STAGE;
+    char* Bs = As + BM * 128;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int c = tid + i * NTHR;
+      *reinterpret_cast<u32x4*>(As + lds_slot(c >> 3, c & 7)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int c = tid + i * NTHR;
+      const int r = c / B_GROW, ch = c % B_GROW;
+      if constexpr (B_I8) {
+        u32x4 lo, hi;
+        i8x16_to_bf16(rb[i], lo, hi);
+        *reinterpret_cast<u32x4*>(Bs + lds_slot(r, 2 * ch)) = lo;
+        *reinterpret_cast<u32x4*>(Bs + lds_slot(r, 2 * ch + 1)) = hi;
+      } else {
+        *reinterpret_cast<u32x4*>(Bs + lds_slot(r, ch)) = rb[i];
+      }
+    }
+  };
+
+  f32x16 acc[MT][NTL];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) acc[i][j] = f32x16{};
+
+  const int arow = wm * WTM + (lane & 31);
+  const int brow = wn * WTN + (lane & 31);
+  const int half = lane >> 5;
+
+  auto compute = [&](int buf) {
+    const char* As = smem + buf * STAGE;
+    const char* Bs = As + BM * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 af[MT], bfr[NTL];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(As + lds_slot(arow + i * 32, 2 * s + half));
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(Bs + lds_slot(brow + j * 32, 2 * s + half));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+          if constexpr (A_F32) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[i][j] = mfma32_f32(__uint_as_float(af[i][t]), __uint_as_float(bfr[j][t]), acc[i][j]);
+          } else {
+            acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]),
+                                    acc[i][j]);
+          }
+        }
+    }
+  };
+
+  const int KT = (int)(g.K / BK);
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_tiles((int64_t)(kt + 1) * BK);
+    compute(cur);
+    if (kt + 1 < KT) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
+  const float* bscale = g.bscale;
+  if constexpr (EPI == EPI_GATEUP) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int p = 0; p < NTL / 2; ++p) {
+        const int64_t f = tn * (BN / 2) + ((wn * NTL + 2 * p) >> 1) * 32 + (lane & 31);
+        float sg = 1.f, su = 1.f;
+        if (bscale) {
+          sg = bscale[f];
+          su = bscale[f + g.up_offset];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < g.M) {
+            const float gv = acc[i][2 * p][r] * sg;
+            const float uv = acc[i][2 * p + 1][r] * su;
+            store_act(static_cast<TA*>(g.out) + row * g.ldo + f, silu_f32(gv) * uv);
+          }
+        }
+      }
+  } else if constexpr (EPI == EPI_STORE_T) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+        const float sc = bscale ? bscale[col] : 1.f;
+        TA* orow = static_cast<TA*>(g.out) + col * g.ldo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t row0 = m0 + wm * WTM + i * 32 + 8 * q + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * sc;
+          if (row0 + 3 < g.M) {
+            if constexpr (sizeof(TA) == 2) {
+              *reinterpret_cast<u32x2*>(orow + row0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+              *reinterpret_cast<f32x4*>(orow + row0) = f32x4{v[0], v[1], v[2], v[3]};
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (row0 + t < g.M) store_act(orow + row0 + t, v[t]);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+        const float sc = bscale ? bscale[col] : 1.f;
+        const float gt = (EPI == EPI_STORE) ? 1.f : g.gate[col];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row >= g.M) continue;
+          const float v = acc[i][j][r] * sc;
+          if constexpr (EPI == EPI_STORE) {
+            store_act(static_cast<TA*>(g.out) + row * g.ldo + col, v);
+          } else if constexpr (EPI == EPI_RESID) {
+            const float xv = load_act(static_cast<const TA*>(g.aux) + row * g.ldaux + col);
+            static_cast<float*>(g.out)[row * g.ldo + col] = xv + gt * v;
+          } else if constexpr (EPI == EPI_ACCUM) {
+            float* o = static_cast<float*>(g.out) + row * g.ldo + col;
+            *o = *o + gt * v;
+          } else {  // EPI_FINAL
+            const float sv = static_cast<const float*>(g.aux)[row * g.ldaux + col];
+            store_act(static_cast<TA*>(g.out) + row * g.ldo + col, sv + gt * v);
+          }
+        }
+      }
+  }
+}
+
+template <typename TA, typename TB, int EPI>
+static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
+  // Tile shape depends only on N (never on M), so every token row takes the
+  // same instruction sequence whatever the slab size.
+  constexpr int BM = 128;
+  const int64_t tiles_m = ceil_div(g.M, BM);
+  if constexpr (EPI == EPI_GATEUP) {
+    if (g.N % 64) return hipErrorInvalidValue;
+    const int64_t tiles = tiles_m * (g.N / 64);
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 128, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+  } else {
+    if (g.N % 128 == 0) {
+      const int64_t tiles = tiles_m * (g.N / 128);
+      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 128, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+    } else if (g.N % 64 == 0) {
+      const int64_t tiles = tiles_m * (g.N / 64);
+      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 64, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename TA, typename TB>
+static hipError_t launch_types(Epilogue epi, const GemmArgs& g, hipStream_t st) {
+  switch (epi) {
+    case EPI_STORE: return launch_epi<TA, TB, EPI_STORE>(g, st);
+    case EPI_STORE_T: return launch_epi<TA, TB, EPI_STORE_T>(g, st);
+    case EPI_RESID: return launch_epi<TA, TB, EPI_RESID>(g, st);
+    case EPI_GATEUP: return launch_epi<TA, TB, EPI_GATEUP>(g, st);
+    case EPI_ACCUM: return launch_epi<TA, TB, EPI_ACCUM>(g, st);
+    case EPI_FINAL: return launch_epi<TA, TB, EPI_FINAL>(g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const int bk = dtype == F32 ? 32 : 64;
+  if (g.K <= 0 || g.K % bk) return hipErrorInvalidValue;
+  switch (dtype) {
+    case F32: return launch_types<float, float>(epi, g, st);
+    case BF16: return launch_types<uint16_t, uint16_t>(epi, g, st);
+    case W8_BF16: return launch_types<uint16_t, int8_t>(epi, g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dit

@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal interface of the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// K1: modulated LayerNorm of `rows` rows of length d (d % 8 == 0, d <= 8192).
+hipError_t launch_modnorm(int in_f32, int out_f32, const void* x, int64_t ldx, const float* shift,
+                          const float* scale, void* out, int64_t ldo, int64_t rows, int d,
+                          float eps, hipStream_t st);
+
+// K2 epilogues.
+enum Epilogue : int {
+  EPI_STORE = 0,    // out[m][n] = acc                        (activation type)
+  EPI_STORE_T = 1,  // out[n][m] = acc                        (transposed store)
+  EPI_RESID = 2,    // out[m][n] (fp32) = aux[m][n] + gate[n] * acc     aux: activation type
+  EPI_GATEUP = 3,   // out[m][f] = silu(acc_gate) * acc_up    (B rows paired gate/up)
+  EPI_ACCUM = 4,    // out[m][n] (fp32) += gate[n] * acc
+  EPI_FINAL = 5,    // out[m][n] = aux[m][n] (fp32) + gate[n] * acc     out: activation type
+};
+
+struct GemmArgs {
+  const void* a;        // [M][K] activations (bf16, or fp32 for the F32 block)
+  int64_t lda;
+  const void* b;        // [N][K] weight rows (bf16, fp32 or int8); GATEUP: first gate row
+  int64_t ldb;
+  const float* bscale;  // int8 weights: fp32 scale per B row (same offset as b), else null
+  int64_t up_offset;    // GATEUP: rows from a gate row to its up row (F)
+  int64_t M, N, K;      // N = output columns (GATEUP: features)
+  void* out;
+  int64_t ldo;
+  const void* aux;      // RESID: x rows; FINAL: fp32 stage rows
+  int64_t ldaux;
+  const float* gate;    // RESID/ACCUM/FINAL: gate vector indexed by output column
+};
+
+// dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
+hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st);
+
+// K3: softmax attention of n_q query rows against n_kv keys for all heads.
+// q [n_q][ldq], k [n_kv][ldk], vt [n_heads*head_dim][ldvt] (V transposed),
+// o [n_q][ldo]; head h owns columns h*head_dim.. of q, k, o and rows of vt.
+hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                            const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q,
+                            int64_t n_kv, int n_heads, int head_dim, hipStream_t st);
+
+}  // namespace dit

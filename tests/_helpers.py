@@ -1,0 +1,71 @@
+"""Shared pieces of the GPU tests: seeded inputs on the device and the oracle on the host."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle.dit_block as O
+from memory_bounded_chunked_amd import block as B
+from memory_bounded_chunked_amd import synth
+
+
+def oracle_inputs(inputs: dict):
+    """x, mod and the fp64 weights the oracle takes, decoded exactly from the stored arrays."""
+    x = synth.to_f64(inputs["x"]) if "x" in inputs else None
+    mod = inputs["mod"].astype(np.float64)
+    w = O.block_weights_f64({k: synth.to_f64(v) for k, v in inputs.items() if k[:2] in ("w_", "s_")})
+    return x, mod, w
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bf16 value (as fp64), for the output-format error floor."""
+    return synth.bf16_bits_to_f64(synth.f64_to_bf16_bits(a))
+
+
+def rel_l2(a, b) -> float:
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(np.asarray(b)), 1e-300))
+
+
+def max_abs(a, b) -> float:
+    return float(np.abs(np.asarray(a) - np.asarray(b)).max())
+
+
+def run_block(shape, inputs, ca, cm, fc=0, poison=False, device="cuda"):
+    """One GPU forward; returns the output as a host tensor (bit patterns preserved)."""
+    blk, x, mod = B.block_from_inputs(shape, inputs, device)
+    nbytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if poison:
+        ws.fill_(0xFF)  # NaN in every fp32 / bf16 lane
+    blk.forward(x, mod, ca, cm, fc, workspace=ws)
+    torch.cuda.synchronize()
+    out = x.cpu()
+    blk.close()
+    return out
+
+
+def bits(t: torch.Tensor) -> bytes:
+    return t.contiguous().view(torch.uint8).numpy().tobytes()
+
+
+def half_ulp_bf16(a: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |a| (2^(e-8) for |a| in [2^e, 2^(e+1)))."""
+    _, e = np.frexp(np.abs(a))
+    return np.ldexp(1.0, e - 9)
+
+
+def check_bf16_bar(y: np.ndarray, y_ref: np.ndarray, max_abs_bar: float = 2e-2, rel_bar: float = 1e-2):
+    """The bf16 parity bar: rel-L2 <= 1e-2; per element |y - y_ref| <= 2e-2 plus the
+    bf16 output's own half-ulp at y_ref (x is bf16 in place, so no output can be
+    closer than that); and elements over the plain 2e-2 at most 1e-5 of all."""
+    err = np.abs(y - y_ref)
+    assert rel_l2(y, y_ref) <= rel_bar, f"rel_l2 {rel_l2(y, y_ref)}"
+    worst = float((err - half_ulp_bf16(y_ref)).max())
+    assert worst <= max_abs_bar, f"max(|err| - half_ulp) = {worst}"
+    over = int((err > max_abs_bar).sum())
+    assert over <= 1e-5 * err.size, f"{over} of {err.size} elements above {max_abs_bar}"
+    return float(err.max()), over

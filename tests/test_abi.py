@@ -1,0 +1,158 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+and validates arguments before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from memory_bounded_chunked_amd import block as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = ["dit_block.h", "dit_block_steps.h", "dit_block_profile.h"]
+
+
+def _declared():
+    names = set()
+    for h in HEADERS:
+        src = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"^(?:const\s+)?\w+\*?\s+\*?(dit_\w+)\(", src, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"dit_block_create", "dit_block_forward", "dit_block_peak_workspace",
+            "dit_modnorm", "dit_attention", "dit_linear", "dit_profile_read"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(B.EXPORTS)
+
+
+def _handle(lib, d=256, heads=2, hd=128, ffn=512, dtype=1, eps=1e-6, wptr=0x10000, scales=True):
+    desc = B._Desc(d, heads, hd, ffn, dtype, eps)
+    s = wptr if scales else 0
+    w = B._Weights(wptr, wptr, wptr, wptr, s, s, s, s)
+    h = ctypes.c_void_p()
+    rc = lib.dit_block_create(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(h))
+    return rc, h
+
+
+def test_create_validation(lib):
+    rc, h = _handle(lib)
+    assert rc == B.DIT_OK and h.value
+    lib.dit_block_destroy(h)
+    bad = [dict(d=250), dict(hd=96, d=192, heads=2), dict(ffn=100), dict(ffn=0), dict(dtype=7),
+           dict(eps=0.0), dict(wptr=0x10008), dict(wptr=0), dict(dtype=2, scales=False), dict(d=16384, heads=128)]
+    for kw in bad:
+        rc, _ = _handle(lib, **kw)
+        assert rc == B.DIT_EINVAL, kw
+
+
+def _ws(lib, h, n, ca, cm, fc):
+    out = ctypes.c_size_t()
+    rc = lib.dit_block_peak_workspace(h, n, ca, cm, fc, ctypes.byref(out))
+    return rc, out.value
+
+
+def _closed_form(n, d, ffn, e, ca, cm, fc):
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    ca = n if ca == 0 else min(ca, n)
+    cm = min(cm, n)
+    fc = ffn if fc == 0 else min(fc, ffn)
+    s = max(ca, cm)
+    np_ = (n + 63) // 64 * 64
+    return (r(n * d * e) + r(d * np_ * e) + r(s * d * 4)
+            + max(2 * r(ca * d * e), r(cm * d * e) + r(cm * fc * e)))
+
+
+@pytest.mark.parametrize("n,ca,cm,fc", [(1000, 256, 256, 0), (1000, 0, 1000, 0), (777, 100, 300, 128),
+                                        (5, 8192, 8192, 0), (32768, 8192, 8192, 0), (131072, 8192, 8192, 3456)])
+def test_workspace_closed_form(lib, n, ca, cm, fc):
+    for dtype, e in ((1, 2), (0, 4), (2, 2)):
+        d, ffn = (5120, 13824) if n >= 32768 else (256, 1024)
+        rc, h = _handle(lib, d=d, heads=d // 128, ffn=ffn, dtype=dtype)
+        assert rc == 0
+        rc, ws = _ws(lib, h, n, ca, cm, fc)
+        assert rc == 0 and ws == _closed_form(n, d, ffn, e, ca, cm, fc)
+        lib.dit_block_destroy(h)
+
+
+def test_workspace_figures_at_32k():
+    # headline block (d=5120, F=13824, N=32768, chunks 8192/8192): K,V 640 MiB,
+    # fp32 staging 160 MiB, slabs max(160, 296) MiB -> 1096 MiB; only K/V grow with N
+    assert _closed_form(32768, 5120, 13824, 2, 8192, 8192, 0) == 1096 * 2 ** 20
+    assert _closed_form(32768, 5120, 13824, 2, 0, 32768, 0) == 2464 * 2 ** 20
+    grow = _closed_form(65536, 5120, 13824, 2, 8192, 8192, 0) - _closed_form(32768, 5120, 13824, 2, 8192, 8192, 0)
+    assert grow == 2 * 32768 * 5120 * 2
+
+
+def test_forward_rejects_before_launch(lib):
+    rc, h = _handle(lib)
+    assert rc == 0
+    _, need = _ws(lib, h, 1000, 256, 256, 0)
+    x, mod, ws = 0x20000, 0x30000, 0x40000
+    f = lib.dit_block_forward
+    cases = [
+        ((None, x, mod, 1000, 256, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, None, mod, 1000, 256, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, None, 1000, 256, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 0, 256, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, -1, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 0, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 256, 100, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 256, -64, ws, need, None), B.DIT_EINVAL),
+        ((h, x + 2, mod, 1000, 256, 256, 0, ws, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 256, 0, ws + 8, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 256, 0, None, need, None), B.DIT_EINVAL),
+        ((h, x, mod, 1000, 256, 256, 0, ws, need - 1, None), B.DIT_ENOSPC),
+        ((h, x, mod, 1000, 256, 256, 0, ws, 0, None), B.DIT_ENOSPC),
+    ]
+    for args, want in cases:
+        assert f(*args) == want, args
+    lib.dit_block_destroy(h)
+
+
+def test_step_entry_points_reject_before_launch(lib):
+    p = 0x10000
+    assert lib.dit_modnorm(1, 1, p, 256, p, p, p, 256, 10, 250, 1e-6, None) == B.DIT_EINVAL
+    assert lib.dit_modnorm(1, 3, p, 256, p, p, p, 256, 10, 256, 1e-6, None) == B.DIT_EINVAL
+    assert lib.dit_modnorm(1, 1, p, 128, p, p, p, 256, 10, 256, 1e-6, None) == B.DIT_EINVAL
+    assert lib.dit_modnorm(1, 1, p, 256, p, p, p, 256, 0, 256, 1e-6, None) == B.DIT_OK  # nothing to do
+    assert lib.dit_attention(1, p, 256, p, 256, p, 64, p, 256, 10, 0, 2, 128, None) == B.DIT_EINVAL
+    assert lib.dit_attention(1, p, 256, p, 256, p, 64, p, 256, 10, 100, 2, 128, None) == B.DIT_EINVAL
+    assert lib.dit_attention(1, p, 256, p, 256, p, 104, p, 256, 10, 100, 2, 96, None) == B.DIT_EINVAL
+    assert lib.dit_attention(2, p, 256, p, 256, p, 104, p, 256, 10, 100, 2, 128, None) == B.DIT_EINVAL
+    assert lib.dit_attention(1, p, 256, p, 256, p, 104, p, 256, 0, 100, 2, 128, None) == B.DIT_OK
+    # dit_linear: k not a multiple of 64, n not a multiple of 64, int8 without scale, missing gate
+    assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 10, 256, 100, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 10, 200, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(2, 0, p, 256, p, 256, None, 0, 10, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(1, 2, p, 256, p, 256, None, 0, 10, 256, 256, p, 256, p, 256, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(1, 3, p, 256, p, 256, None, 100, 10, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+
+
+def test_profile_read_without_records(lib):
+    assert lib.dit_profile_enable(1) == 0
+    t, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.dit_profile_read(3, ctypes.byref(t), ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.dit_profile_read(9, ctypes.byref(t), ctypes.byref(n)) == B.DIT_EINVAL
+    assert lib.dit_profile_enable(0) == 0
+
+
+def test_strerror(lib):
+    assert B.strerror(B.DIT_ENOSPC) == "workspace too small"
+    assert B.strerror(B.DIT_EINVAL) == "invalid argument"
+
+
+def test_defaults_follow_the_pages():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "chunk_knobs.json")))
+    assert B.DEFAULT_ATTN_CHUNK == g["attn_chunk_tokens"]["default"]
+    assert B.DEFAULT_MLP_CHUNK == g["mlp_chunk_tokens"]["default"]

@@ -1,0 +1,137 @@
+"""Whole-block parity of the HIP path against the fp64 oracle, and the
+bit-identity, determinism and bounded-workspace properties (GPU).
+
+Bars: the fp32 block max-abs and rel-L2 1e-4 on y. bf16 blocks rel-L2 1e-2 on
+y, and per element max-abs 2e-2 beyond the bf16 output's own half-ulp, with
+elements over the plain 2e-2 rarer than 1e-5 (``check_bf16_bar``).
+Bit-identity: output bytes equal for every (attn_chunk_tokens,
+mlp_chunk_tokens) at fixed ffn_chunk_features ("LayerStream: H3 Chunking":
+chunked output is bit-identical to the unchunked run).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.dit_block as O
+from _helpers import bf16_round, bits, check_bf16_bar, max_abs, oracle_inputs, rel_l2, run_block, to_f64
+from memory_bounded_chunked_amd import block as B
+from memory_bounded_chunked_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "bf16": synth.BlockShape("small-bf16", 256, 2, 128, 512, 777, "bf16"),
+    "f32": synth.CONFIGS["tiny"],
+    "w8_bf16": synth.BlockShape("small-w8", 256, 2, 128, 512, 611, "w8_bf16"),
+    "bf16-dh64": synth.BlockShape("small-dh64", 256, 4, 64, 768, 450, "bf16"),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def case(request):
+    shape = SMALL[request.param]
+    inputs = synth.make_inputs(shape, seed=0)
+    x, mod, w = oracle_inputs(inputs)
+    y_ref = O.block_forward(x, mod, w, shape.n_heads)
+    return shape, inputs, x, y_ref
+
+
+def test_block_matches_oracle(case):
+    shape, inputs, x, y_ref = case
+    y = to_f64(run_block(shape, inputs, 256, 256))
+    if shape.dtype == "f32":
+        assert max_abs(y, y_ref) <= 1e-4
+        assert rel_l2(y, y_ref) <= 1e-4
+        assert rel_l2(y - x, y_ref - x) <= 1e-4
+    else:
+        check_bf16_bar(y, y_ref)
+        # no worse than twice the error of rounding the exact output to bf16
+        assert rel_l2(y, y_ref) <= 2.0 * rel_l2(bf16_round(y_ref), y_ref)
+
+
+def test_bit_identical_across_chunks(case):
+    shape, inputs, _, _ = case
+    n = shape.n_tokens
+    ref = bits(run_block(shape, inputs, 0, n))
+    for ca, cm in ((256, 256), (100, 300), (64, n), (n, 64), (1, 999), (n - 1, 129)):
+        assert bits(run_block(shape, inputs, ca, cm)) == ref, (ca, cm)
+
+
+def test_deterministic_and_poisoned_workspace(case):
+    shape, inputs, _, _ = case
+    a = bits(run_block(shape, inputs, 128, 192))
+    assert bits(run_block(shape, inputs, 128, 192)) == a
+    assert bits(run_block(shape, inputs, 128, 192, poison=True)) == a
+
+
+def test_ffn_feature_slices_within_tolerance(case):
+    shape, inputs, x, y_ref = case
+    if shape.dtype == "f32":
+        fcs = (128, 320)
+        tol = 1e-4
+    else:
+        fcs = (64, 192)
+    for fc in fcs:
+        y = to_f64(run_block(shape, inputs, 256, 256, fc))
+        if shape.dtype == "f32":
+            assert max_abs(y, y_ref) <= tol and rel_l2(y, y_ref) <= 1e-4
+        else:
+            check_bf16_bar(y, y_ref)
+        # feature slicing is bit-identical across token chunks at fixed fc
+        assert bits(run_block(shape, inputs, 100, 77, fc)) == bits(run_block(shape, inputs, 256, 256, fc))
+
+
+def test_no_hidden_allocation():
+    shape = SMALL["bf16"]
+    inputs = synth.make_inputs(shape, 0)
+    blk, x, mod = B.block_from_inputs(shape, inputs, "cuda")
+    ws = torch.empty(blk.peak_workspace(shape.n_tokens, 128, 128), dtype=torch.uint8, device="cuda")
+    blk.forward(x, mod, 128, 128, workspace=ws)
+    torch.cuda.synchronize()
+    alloc0 = torch.cuda.memory_allocated()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        blk.forward(x, mod, 128, 128, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == alloc0
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+
+
+def test_error_paths_on_device():
+    shape = SMALL["bf16"]
+    inputs = synth.make_inputs(shape, 0)
+    blk, x, mod = B.block_from_inputs(shape, inputs, "cuda")
+    need = blk.peak_workspace(shape.n_tokens, 128, 128)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    before = x.clone()
+    with pytest.raises(B.DitError) as e:
+        blk.forward(x, mod, 128, 128, workspace=ws[: need - 1])
+    assert e.value.code == B.DIT_ENOSPC
+    with pytest.raises(B.DitError) as e:
+        blk.forward(x, mod, 128, 0, workspace=ws)
+    assert e.value.code == B.DIT_EINVAL
+    with pytest.raises(B.DitError) as e:
+        blk.forward(x, mod, 128, 128, 100, workspace=ws)
+    assert e.value.code == B.DIT_EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)  # nothing was enqueued
+
+
+def test_closed_forms_on_device():
+    shape = SMALL["bf16"]
+    inputs = synth.make_inputs(shape, 0)
+    # zero gates: y == x bitwise
+    z = dict(inputs)
+    z["mod"] = inputs["mod"].copy()
+    z["mod"][2] = 0.0
+    z["mod"][5] = 0.0
+    y = run_block(shape, z, 256, 256)
+    assert bits(y) == bits(B.tensor_from_stored(inputs["x"], "cpu"))
+    # one token: o == v, so the block equals the oracle's one-token block
+    one = shape.replace(n_tokens=1)
+    inp1 = dict(inputs)
+    inp1["x"] = inputs["x"][:1].copy()
+    x, mod, w = oracle_inputs(inp1)
+    y1 = to_f64(run_block(one, inp1, 0, 1))
+    check_bf16_bar(y1, O.block_forward(x, mod, w, one.n_heads))

@@ -1,0 +1,210 @@
+"""Per-kernel parity of the HIP steps against the fp64 oracle (GPU).
+
+Each kernel is called through its C-ABI step entry point on seeded inputs
+whose sizes span several tiles and end in ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.dit_block as O
+from _helpers import bf16_round, max_abs, rel_l2, to_f64
+from memory_bounded_chunked_amd import block as B
+from memory_bounded_chunked_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bf16(a: np.ndarray) -> torch.Tensor:
+    return B.tensor_from_stored(synth.f64_to_bf16_bits(a), DEV)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+@pytest.mark.parametrize("rows,d", [(1, 256), (37, 256), (1000, 3072), (515, 5120)])
+def test_modnorm_bf16(rows, d):
+    rng = _rng(rows + d)
+    x = synth.bf16_bits_to_f64(synth.f64_to_bf16_bits(rng.standard_normal((rows, d)) * 1.7 + 0.3))
+    sh = (rng.standard_normal(d) * 0.3).astype(np.float32)
+    sc = (rng.standard_normal(d) * 0.3).astype(np.float32)
+    out = torch.empty(rows, d, dtype=torch.bfloat16, device=DEV)
+    B.modnorm(_bf16(x), torch.from_numpy(sh).to(DEV), torch.from_numpy(sc).to(DEV), out)
+    ref = O.modulate(O.layer_norm(x, 1e-6), sh.astype(np.float64), sc.astype(np.float64))
+    got = to_f64(out)
+    # bf16 output: within half an ulp of the reference plus fp32 statistics error
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5)
+
+
+@pytest.mark.parametrize("in_f32,out_f32", [(True, True), (True, False)])
+def test_modnorm_f32_input(in_f32, out_f32):
+    rows, d = 300, 1024
+    rng = _rng(3)
+    x = rng.standard_normal((rows, d)).astype(np.float32) * 2.0
+    sh = (rng.standard_normal(d) * 0.3).astype(np.float32)
+    sc = (rng.standard_normal(d) * 0.3).astype(np.float32)
+    out = torch.empty(rows, d, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    B.modnorm(torch.from_numpy(x).to(DEV), torch.from_numpy(sh).to(DEV), torch.from_numpy(sc).to(DEV), out)
+    ref = O.modulate(O.layer_norm(x.astype(np.float64), 1e-6), sh.astype(np.float64), sc.astype(np.float64))
+    got = to_f64(out)
+    tol = 1e-5 if out_f32 else 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * tol + 1e-5)
+
+
+def _linear_case(dtype, m, n, k, seed, rows_w=None):
+    rng = _rng(seed)
+    rows_w = n if rows_w is None else rows_w
+    a = rng.standard_normal((m, k))
+    if dtype == "f32":
+        a = a.astype(np.float32).astype(np.float64)
+        w = (rng.standard_normal((rows_w, k)) / np.sqrt(k)).astype(np.float32).astype(np.float64)
+        ta, tw, ts, wf = (torch.from_numpy(a.astype(np.float32)).to(DEV),
+                          torch.from_numpy(w.astype(np.float32)).to(DEV), None, w)
+    elif dtype == "bf16":
+        a = bf16_round(a)
+        w = bf16_round(rng.standard_normal((rows_w, k)) / np.sqrt(k))
+        ta, tw, ts, wf = _bf16(a), _bf16(w), None, w
+    else:
+        a = bf16_round(a)
+        q = rng.integers(-127, 127, size=(rows_w, k), endpoint=True, dtype=np.int8)
+        s = rng.uniform(1e-4, 1e-3, rows_w).astype(np.float32)
+        wf = O.dequantize_rows(q, s)
+        ta, tw, ts = _bf16(a), torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
+    return a, wf, ta, tw, ts
+
+
+def _act_dtype(dtype):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def _out_tol(dtype):
+    return 1e-5 if dtype == "f32" else 2.0 ** -8
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (300, 384, 512), (129, 256, 256)])
+def test_linear_store(dtype, m, n, k):
+    a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, m + n + k)
+    out = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "store", ta, tw, out, n, w_scale=ts)
+    ref = O.linear(a, wf)
+    scale = np.abs(ref).max()
+    assert np.all(np.abs(to_f64(out) - ref) <= np.abs(ref) * _out_tol(dtype) + 1e-5 * scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+def test_linear_store_transposed(dtype):
+    m, n, k, ld = 203, 128, 256, 256
+    a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 11)
+    out = torch.zeros(n, ld, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "store_t", ta, tw, out, n, w_scale=ts)
+    ref = O.linear(a, wf).T
+    got = to_f64(out)
+    scale = np.abs(ref).max()
+    assert np.all(np.abs(got[:, :m] - ref) <= np.abs(ref) * _out_tol(dtype) + 1e-5 * scale)
+    assert np.all(got[:, m:] == 0)  # nothing written past the last token
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+def test_linear_residual_epilogues(dtype):
+    m, n, k = 333, 256, 512
+    a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 12)
+    rng = _rng(13)
+    x = rng.standard_normal((m, n))
+    x = x.astype(np.float32).astype(np.float64) if dtype == "f32" else bf16_round(x)
+    tx = torch.from_numpy(x.astype(np.float32)).to(DEV) if dtype == "f32" else _bf16(x)
+    gate = (rng.standard_normal(n) * 0.3).astype(np.float32)
+    tg = torch.from_numpy(gate).to(DEV)
+    acc = O.linear(a, wf)
+    g64 = gate.astype(np.float64)
+    # RESID: stage = x + gate * acc (fp32)
+    stage = torch.empty(m, n, dtype=torch.float32, device=DEV)
+    B.linear(dtype, "resid", ta, tw, stage, n, w_scale=ts, aux=tx, gate=tg)
+    ref = x + g64 * acc
+    assert max_abs(to_f64(stage), ref) <= 1e-5 * np.abs(ref).max()
+    # ACCUM: stage += gate * acc
+    base = to_f64(stage)
+    B.linear(dtype, "accum", ta, tw, stage, n, w_scale=ts, gate=tg)
+    ref2 = base + g64 * acc
+    assert max_abs(to_f64(stage), ref2) <= 1e-5 * np.abs(ref2).max()
+    # FINAL: out = stage + gate * acc, rounded once to the activation type
+    out = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "final", ta, tw, out, n, w_scale=ts, aux=stage, gate=tg)
+    ref3 = ref2 + g64 * acc
+    got = to_f64(out)
+    assert np.all(np.abs(got - ref3) <= np.abs(ref3) * _out_tol(dtype) + 1e-5 * np.abs(ref3).max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+def test_linear_gateup(dtype):
+    m, f, k = 301, 192, 256
+    a, wf, ta, tw, ts = _linear_case(dtype, m, f, k, 14, rows_w=2 * f)
+    out = torch.empty(m, f, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "gateup", ta, tw, out, f, w_scale=ts, up_offset=f)
+    ref = O.silu(O.linear(a, wf[:f])) * O.linear(a, wf[f:])
+    got = to_f64(out)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * _out_tol(dtype) + 1e-4 * np.abs(ref).max())
+    # a feature slice [64, 192) addressed through the weight pointer offset
+    sub = torch.empty(m, 128, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "gateup", ta, tw[64:], sub, 128, w_scale=None if ts is None else ts[64:], up_offset=f)
+    torch.cuda.synchronize()
+    assert torch.equal(sub.cpu(), out[:, 64:].cpu())
+
+
+def _attn_inputs(dtype, n_q, n_kv, heads, dh, seed, scale=1.0):
+    rng = _rng(seed)
+    d = heads * dh
+    q, k, v = (rng.standard_normal((n, d)) * scale for n in (n_q, n_kv, n_kv))
+    ld_vt = (n_kv + 63) // 64 * 64
+    if dtype == "f32":
+        q, k, v = (t.astype(np.float32).astype(np.float64) for t in (q, k, v))
+        mk = lambda a: torch.from_numpy(a.astype(np.float32)).to(DEV)  # noqa: E731
+        tdt = torch.float32
+    else:
+        q, k, v = (bf16_round(t) for t in (q, k, v))
+        mk = _bf16
+        tdt = torch.bfloat16
+    vt = torch.zeros(d, ld_vt, dtype=tdt, device=DEV)
+    vt[:, :n_kv] = mk(v).T
+    return q, k, v, mk(q), mk(k), vt, tdt
+
+
+@pytest.mark.parametrize("dtype,heads,dh,n_q,n_kv", [
+    ("bf16", 3, 128, 300, 1000), ("bf16", 2, 128, 1, 1), ("bf16", 2, 128, 129, 64),
+    ("bf16", 2, 64, 257, 333), ("f32", 4, 64, 300, 1000), ("f32", 2, 64, 5, 7), ("f32", 2, 128, 70, 200)])
+def test_attention(dtype, heads, dh, n_q, n_kv):
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs(dtype, n_q, n_kv, heads, dh, n_q * 7 + n_kv)
+    out = torch.empty(n_q, heads * dh, dtype=tdt, device=DEV)
+    B.attention(tq, tk, tvt, out, heads, n_kv=n_kv)
+    ref = O.attention(q, k, v, heads)
+    got = to_f64(out)
+    if dtype == "f32":
+        assert max_abs(got, ref) <= 1e-5 * max(1.0, np.abs(ref).max())
+    else:
+        assert rel_l2(got, ref) <= 1e-2
+        assert max_abs(got, ref) <= 2e-2 * max(np.abs(ref).max(), 1e-3)
+        # no worse than twice what rounding the exact result to bf16 costs, plus P's rounding
+        assert rel_l2(got, ref) <= 2 * rel_l2(bf16_round(ref), ref) + 4e-3
+
+
+def test_attention_sharp_logits():
+    # large logits (near one-hot softmax) exercise the running max and rescaling
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", 200, 700, 2, 128, 5, scale=3.0)
+    out = torch.empty(200, 256, dtype=tdt, device=DEV)
+    B.attention(tq, tk, tvt, out, 2, n_kv=700)
+    ref = O.attention(q, k, v, 2)
+    assert rel_l2(to_f64(out), ref) <= 1e-2
+
+
+def test_attention_query_slices_bit_identical():
+    n_q, n_kv = 400, 900
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, 2, 128, 21)
+    full = torch.empty(n_q, 256, dtype=tdt, device=DEV)
+    B.attention(tq, tk, tvt, full, 2, n_kv=n_kv)
+    for a, b in ((0, 1), (1, 130), (77, 400), (128, 256)):
+        part = torch.empty(b - a, 256, dtype=tdt, device=DEV)
+        B.attention(tq[a:b], tk, tvt, part, 2, n_kv=n_kv)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
