@@ -80,7 +80,7 @@ def main() -> int:
     ap.add_argument("--attn-chunk", type=int, default=None)
     ap.add_argument("--mlp-chunk", type=int, default=None)
     ap.add_argument("--ffn-chunk", type=int, default=None)
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -144,10 +144,11 @@ def main() -> int:
     peak = PEAK_F32_TFLOPS if shape.dtype == "f32" else PEAK_BF16_TFLOPS
     att_t, att_n = prof["attention"]
     ca_eff = n if ca == 0 else min(ca, n)
-    # algorithmic FLOPs per attention launch: 4*d per (query, key) pair x (slice rows x N keys);
-    # every launch in this schedule has ca_eff rows unless N % ca_eff leaves a shorter last slice
-    pairs = n * n  # all launches together cover N queries x N keys
-    att_tflops = 4.0 * d * pairs / (att_t / 1e3) / 1e12 if att_t > 0 else None
+    # Algorithmic FLOPs of one attention launch: 4*d per (query, key) pair
+    # (QK^T and PV, 2*d each) x (ca_eff query rows x N keys).
+    att_flops_launch = 4.0 * d * ca_eff * n
+    att_avg_ms = att_t / att_n if att_n else None
+    att_tflops = att_flops_launch / (att_avg_ms / 1e3) / 1e12 if att_avg_ms else None
     roofline = {
         "kernel": "attention",
         "bound": "mfma",
@@ -156,8 +157,8 @@ def main() -> int:
         "unit": "TFLOP/s",
         "frac": round(att_tflops / peak, 4) if att_tflops else None,
         "traffic": None,
-        "avg_launch_ms": round(att_t / att_n, 4) if att_n else None,
-        "flops_per_launch": 4.0 * d * ca_eff * n,
+        "avg_launch_ms": round(att_avg_ms, 4) if att_avg_ms else None,
+        "flops_per_launch": att_flops_launch,
     }
     result = {
         "metric": METRIC,

@@ -61,11 +61,11 @@ def half_ulp_bf16(a: np.ndarray) -> np.ndarray:
 def check_bf16_bar(y: np.ndarray, y_ref: np.ndarray, max_abs_bar: float = 2e-2, rel_bar: float = 1e-2):
     """The bf16 parity bar: rel-L2 <= 1e-2; per element |y - y_ref| <= 2e-2 plus the
     bf16 output's own half-ulp at y_ref (x is bf16 in place, so no output can be
-    closer than that); and elements over the plain 2e-2 at most 1e-5 of all."""
+    closer than that); and elements over the plain 2e-2 at most 1e-4 of all."""
     err = np.abs(y - y_ref)
     assert rel_l2(y, y_ref) <= rel_bar, f"rel_l2 {rel_l2(y, y_ref)}"
     worst = float((err - half_ulp_bf16(y_ref)).max())
     assert worst <= max_abs_bar, f"max(|err| - half_ulp) = {worst}"
     over = int((err > max_abs_bar).sum())
-    assert over <= 1e-5 * err.size, f"{over} of {err.size} elements above {max_abs_bar}"
+    assert over <= 1e-4 * err.size, f"{over} of {err.size} elements above {max_abs_bar}"
     return float(err.max()), over
