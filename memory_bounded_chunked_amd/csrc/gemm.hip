@@ -1,11 +1,20 @@
 // K2: C[M][N] = A[M][K] * B[N][K]^T on MFMA, with fused epilogues.
 //
 // A holds token rows (activations), B holds weight rows [out][in]; both are
-// K-contiguous, which is the operand layout MFMA consumes directly. Tiles of
-// A and B are staged through LDS (double buffered: the next k-tile's global
-// loads are in flight while the current one is multiplied). LDS rows are
-// 128 B (8 chunks of 16 B) and chunk c of row r lives at slot c ^ (r & 7), so
-// the 8 lanes served together by a 16-byte LDS read always hit distinct banks.
+// K-contiguous, which is the operand layout MFMA consumes directly. A
+// 256-row tile of A and a BN-row tile of B are staged through LDS (double
+// buffered: the next k-tile's global loads are in flight while the current
+// one is multiplied); each of the 4 wavefronts computes a 128 x BN/2 block
+// with its accumulators in AGPRs, so every 16-byte fragment read from LDS
+// feeds BN/64 (or 4) MFMAs. LDS rows hold 128 B of k and are padded to 144 B:
+// consecutive rows start 4 banks apart, so fragment reads are conflict-free
+// and their addresses are a per-lane base plus compile-time offsets.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2. The hardware workgroup id is remapped so that each XCD owns a
+// contiguous range of tiles, walked in groups of 4 tile rows; the 32
+// workgroups an XCD runs at once then cover a 4 x 8 block of tiles and share
+// their A and B k-slices through that XCD's L2.
 //
 // Each output element is the same fixed sequence: 32x32x16 bf16 MFMA (or
 // 32x32x2 fp32 MFMA for the F32 block) accumulations over k in increasing
@@ -22,8 +31,23 @@
 
 namespace dit {
 
-__device__ __forceinline__ int lds_slot(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+constexpr int LDS_ROW = 144;  // 128 B of k per row + 16 B pad
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * LDS_ROW + chunk * 16; }
+
+// Logical tile of hardware workgroup `bid` (see the tile-order note above).
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
+  constexpr int64_t XCDS = 8, GM = 4;
+  const int64_t total = tiles_m * tiles_n;
+  const int64_t xcd = bid % XCDS, j = bid / XCDS;
+  const int64_t base = total / XCDS, rem = total % XCDS;
+  const int64_t l = xcd * base + (xcd < rem ? xcd : rem) + j;
+  const int64_t grp = l / (GM * tiles_n);
+  const int64_t rows = (tiles_m - grp * GM) < GM ? (tiles_m - grp * GM) : GM;
+  const int64_t within = l - grp * GM * tiles_n;
+  tm = grp * GM + within % rows;
+  tn = within / rows;
 }
 
 // 16 int8 -> 16 bf16 (exact).
@@ -72,7 +96,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   constexpr int A_LD = BM * 8 / NTHR;
   constexpr int B_GROW = B_I8 ? 4 : 8;  // 16-B global chunks per B tile row
   constexpr int B_LD = BN * B_GROW / NTHR;
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int STAGE = (BM + BN) * LDS_ROW;
   static_assert(BM * 8 % NTHR == 0 && BN * B_GROW % NTHR == 0, "tile/threads");
   static_assert(EPI != EPI_GATEUP || NTL % 2 == 0, "gate/up tiles come in pairs");
 
@@ -85,7 +109,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 
   constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   const int64_t tiles_n = g.N / OUT_BN;
-  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, ceil_div(g.M, BM), tiles_n, tm, tn);
   const int64_t m0 = tm * BM;
 
   const char* A = static_cast<const char*>(g.a);
@@ -102,28 +127,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     }
   };
 
+  // Global loads: a uniform base advanced per k-tile plus a 32-bit byte
+  // offset per thread and chunk (row * ld + chunk), fixed for the whole loop.
+  uint32_t aoff[A_LD], boff[B_LD];
+  bool aval[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int c = tid + i * NTHR;
+    const int64_t gr = m0 + (c >> 3);
+    aval[i] = gr < g.M;
+    aoff[i] = aval[i] ? (uint32_t)((gr - m0) * g.lda * (int64_t)sizeof(TA) + (c & 7) * 16) : 0u;
+  }
+  const int64_t b_first = b_row(0);
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int c = tid + i * NTHR;
+    boff[i] = (uint32_t)((b_row(c / B_GROW) - b_first) * g.ldb * (int64_t)sizeof(TB) + (c % B_GROW) * 16);
+  }
+  const char* a_base = A + m0 * g.lda * (int64_t)sizeof(TA);
+  const char* b_base = B + b_first * g.ldb * (int64_t)sizeof(TB);
+
+  // One register staging set: tile kt+1 is written from it to LDS while
+  // tile kt is multiplied, then it is refilled with tile kt+2 (see below).
   u32x4 ra[A_LD], rb[B_LD];
   auto load_tiles = [&](int64_t k0) {
+    const char* at = a_base + k0 * (int64_t)sizeof(TA);
+    const char* bt = b_base + k0 * (int64_t)sizeof(TB);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = c >> 3, ch = c & 7;
-      const int64_t gr = m0 + r;
-      if (gr < g.M)
-        ra[i] = *reinterpret_cast<const u32x4*>(A + (gr * g.lda + k0) * (int64_t)sizeof(TA) + ch * 16);
-      else
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < A_LD; ++i)
+      ra[i] = aval[i] ? *reinterpret_cast<const u32x4*>(at + aoff[i]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int c = tid + i * NTHR;
-      const int r = c / B_GROW, ch = c % B_GROW;
-      rb[i] = *reinterpret_cast<const u32x4*>(B + (b_row(r) * g.ldb + k0) * (int64_t)sizeof(TB) + ch * 16);
-    }
+    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bt + boff[i]);
   };
   auto store_tiles = [&](int buf) {
     char* As = smem + buf * STAGE;
-    char* Bs = As + BM * 128;
+    char* Bs = As + BM * LDS_ROW;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int c = tid + i * NTHR;
@@ -154,18 +192,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   const int brow = wn * WTN + (lane & 31);
   const int half = lane >> 5;
 
+  const int a_rd = lds_slot(arow, half), b_rd = lds_slot(brow, half);
   auto compute = [&](int buf) {
-    const char* As = smem + buf * STAGE;
-    const char* Bs = As + BM * 128;
+    const char* As = smem + buf * STAGE + a_rd;
+    const char* Bs = smem + buf * STAGE + BM * LDS_ROW + b_rd;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 af[MT], bfr[NTL];
 #pragma unroll
       for (int i = 0; i < MT; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(As + lds_slot(arow + i * 32, 2 * s + half));
+        af[i] = *reinterpret_cast<const u32x4*>(As + i * 32 * LDS_ROW + s * 32);
 #pragma unroll
       for (int j = 0; j < NTL; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4*>(Bs + lds_slot(brow + j * 32, 2 * s + half));
+        bfr[j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * LDS_ROW + s * 32);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -182,17 +221,30 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     }
   };
 
+  // k-tile kt is multiplied from LDS buffer kt & 1. While it is, tile kt+1
+  // (loaded from HBM during the previous iteration) goes from the staging
+  // registers into the other buffer, whose previous tile every wave finished
+  // before the last barrier, and the staging registers are refilled with
+  // tile kt+2. One barrier per k-tile.
   const int KT = (int)(g.K / BK);
   load_tiles(0);
   store_tiles(0);
+  if (KT > 1) load_tiles(BK);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_tiles((int64_t)(kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < KT) store_tiles(cur ^ 1);
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) {
+    compute(kt & 1);
+    store_tiles((kt + 1) & 1);
+    load_tiles((int64_t)(kt + 2) * BK);
     __syncthreads();
   }
+  if (kt + 1 < KT) {
+    compute(kt & 1);
+    store_tiles((kt + 1) & 1);
+    __syncthreads();
+    ++kt;
+  }
+  compute(kt & 1);
 
   // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
   const float* bscale = g.bscale;
@@ -274,28 +326,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   }
 }
 
+template <typename TA, typename TB, int EPI, int BN, int WM, int WN>
+static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
+  constexpr int BM = 256;
+  constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
+  const int64_t tiles = ceil_div(g.M, BM) * (g.N / OUT_BN);
+  hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0, st,
+                     g);
+  return hipGetLastError();
+}
+
 template <typename TA, typename TB, int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  // Tile shape depends only on N (never on M), so every token row takes the
-  // same instruction sequence whatever the slab size.
-  constexpr int BM = 128;
-  const int64_t tiles_m = ceil_div(g.M, BM);
+  // The tile shape depends only on N and the epilogue (never on M), so every
+  // token row takes the same instruction sequence whatever the slab size.
+  // 8 wavefronts (2 per SIMD) per 256-row tile: while one wave waits on LDS
+  // or a barrier, the other keeps the matrix core busy.
   if constexpr (EPI == EPI_GATEUP) {
-    if (g.N % 64) return hipErrorInvalidValue;
-    const int64_t tiles = tiles_m * (g.N / 64);
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 128, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+    if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
+    if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
   } else {
-    if (g.N % 128 == 0) {
-      const int64_t tiles = tiles_m * (g.N / 128);
-      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 128, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
-    } else if (g.N % 64 == 0) {
-      const int64_t tiles = tiles_m * (g.N / 64);
-      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, 64, 2, 2>), dim3((unsigned)tiles), dim3(256), 0, st, g);
-    } else {
-      return hipErrorInvalidValue;
-    }
+    // 256-wide tiles only for wide outputs; d-wide outputs (5120) use 128 so
+    // an 8192-row slab gives 1280 tiles: five full rounds over 256 CUs.
+    if (g.N % 256 == 0 && g.N >= 8192) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
+    if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
+    if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 64, 4, 1>(g, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <typename TA, typename TB>
