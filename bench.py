@@ -27,6 +27,20 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+def measured_traffic() -> float | None:
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE measurement, if the kernel sources are still the measured ones."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_large_32k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -156,7 +170,7 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(att_tflops / peak, 4) if att_tflops else None,
-        "traffic": None,
+        "traffic": measured_traffic() if args.config == "large" and (ca, cm, fc) == (8192, 8192, 0) else None,
         "avg_launch_ms": round(att_avg_ms, 4) if att_avg_ms else None,
         "flops_per_launch": att_flops_launch,
     }

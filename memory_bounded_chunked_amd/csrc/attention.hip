@@ -29,6 +29,9 @@
 namespace dit {
 
 constexpr int ATT_BN = 64;  // keys per tile
+#ifndef DIT_ATT_NW
+#define DIT_ATT_NW 8  // wavefronts per workgroup of the bf16 kernel
+#endif
 
 template <typename T, int DH, int NW>
 struct AttLayout {
@@ -299,9 +302,10 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
 // tile t+1 and V tile t, and refills the K slot of tile t (consumed one
 // iteration earlier) with tile t+2 and the V slot of tile t-1 with tile t+1.
 // The row sum is accumulated from the bf16-rounded P that enters the PV
-// product (v_dot2_f32_bf16 against 1.0), two elements per instruction.
+// product (v_dot2_f32_bf16 against 1.0), two elements per instruction, and O
+// is rescaled only when a running max grows by more than 2^8.
 template <int DH, int NW>
-__global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_bf16_kernel(const uint16_t* __restrict__ q, int64_t ldq,
                                                                  const uint16_t* __restrict__ k, int64_t ldk,
                                                                  const uint16_t* __restrict__ vt, int64_t ldvt,
                                                                  uint16_t* __restrict__ o, int64_t ldo,
@@ -311,6 +315,12 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t*
   constexpr int K_TILE = L::K_TILE, V_TILE = L::V_TILE, K_LD = L::K_LD, V_LD = L::V_LD;
   constexpr int QS = L::QS, OT = L::OT, NTHR = L::NTHR;
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  // Head-major order, contiguous per XCD: the query tiles of one head run on
+  // one XCD at the same time and share that head's K/V tiles through its L2,
+  // so each head's K/V crosses from HBM about once per launch.
+  const int64_t q_tiles = ceil_div(n_q, L::BM);
+  const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);  // gridDim.x = q_tiles * heads
+  const int64_t head_idx = logical / q_tiles, q_tile = logical % q_tiles;
 
   __shared__ __attribute__((aligned(16))) char smem[2 * K_TILE + 2 * V_TILE];
   char* const kring = smem;
@@ -318,9 +328,8 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t*
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.y;
-  const int64_t q0 = (int64_t)blockIdx.x * L::BM + wave * 32;
-  const int64_t col0 = (int64_t)head * DH;
+  const int64_t q0 = q_tile * L::BM + wave * 32;
+  const int64_t col0 = head_idx * DH;
 
   u32x4 qf[QS];
   {
@@ -428,23 +437,36 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t*
   float m_run = -INFINITY, l_run = 0.f;
   const bf2 ones = __builtin_bit_cast(bf2, 0x3f803f80u);
 
-  // softmax of one tile into packed bf16 P (4 groups of 8 keys x this lane's query)
-  auto softmax = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
+  // Softmax of one tile, in two parts. rescale(): the tile's row max; if
+  // some query's max grew by more than 8 (log2 units) past the max in use,
+  // the whole wave moves to the new maxima and rescales O and the row sums.
+  // Otherwise the stale max stays in use and P may reach 2^8, which fp32
+  // and bf16 hold without loss of relative precision. This is exact up to
+  // rounding, depends only on the query's own scores (not on the slicing),
+  // and happens a handful of times per query. exp_tile(): P = exp2 of the
+  // scaled scores minus the max in use, packed to bf16, and the row sum
+  // accumulated from the packed values.
+  auto rescale = [&](f32x16 (&s)[2]) {
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale_log2);
-    m_run = m_new;
-    const float mc = m_new * qk_scale_log2;
-    float lsum = l_run * alpha;
+    if (__any((mx - m_run) * qk_scale_log2 > 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int t = 0; t < OT; ++t)
+      for (int t = 0; t < OT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[t][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc_o[t][r] *= alpha;
+    }
+  };
+  auto exp_tile = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
+    const float mc = m_run * qk_scale_log2;
+    float lsum = l_run;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x16& sv = s[j >> 1];
@@ -460,6 +482,10 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t*
       pb[j] = u32x4{w[0], w[1], w[2], w[3]};
     }
     l_run = lsum;
+  };
+  auto softmax = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
+    rescale(s);
+    exp_tile(s, pb);
   };
 
   auto pv = [&](int slot, const u32x4 (&pb)[4]) {
@@ -491,8 +517,9 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(const uint16_t*
     if (more_k) load_k(t + 2);
     load_v(t + 1);
     u32x4 pb[4];
+    rescale(s_cur);
     scores((int)((t + 1) & 1), s_nxt);
-    softmax(s_cur, pb);
+    exp_tile(s_cur, pb);
 #pragma unroll
     for (int i = 0; i < QS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS fragment reads
@@ -556,7 +583,8 @@ static hipError_t launch_att_bf16(const void* q, int64_t ldq, const void* k, int
                                   int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int n_heads,
                                   hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  dim3 grid((unsigned)ceil_div(n_q, AttLayout<uint16_t, DH, NW>::BM), (unsigned)n_heads), block(NW * 64);
+  // one-dimensional grid: the kernel derives (head, query tile) from blockIdx.x
+  dim3 grid((unsigned)(ceil_div(n_q, AttLayout<uint16_t, DH, NW>::BM) * n_heads)), block(NW * 64);
   hipLaunchKernelGGL((attention_bf16_kernel<DH, NW>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
                      static_cast<const uint16_t*>(k), ldk, static_cast<const uint16_t*>(vt), ldvt,
                      static_cast<uint16_t*>(o), ldo, n_q, n_kv, scale_log2);
@@ -584,8 +612,8 @@ hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k
     if (head_dim == 64) return launch_att_t<float, 64, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
     if (head_dim == 128) return launch_att_t<float, 128, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
   } else {
-    if (head_dim == 64) return launch_att_bf16<64, 8>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
-    if (head_dim == 128) return launch_att_bf16<128, 8>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 64) return launch_att_bf16<64, DIT_ATT_NW>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 128) return launch_att_bf16<128, DIT_ATT_NW>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
   }
   return hipErrorInvalidValue;
 }

@@ -46,6 +46,16 @@ __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) 
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+// hardware id b runs on XCD b % 8. This maps b to a logical id so that every
+// XCD owns one contiguous range of logical ids (a bijection on [0, total)).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t total) {
+  constexpr int64_t XCDS = 8;
+  const int64_t xcd = b % XCDS, j = b / XCDS;
+  const int64_t base = total / XCDS, rem = total % XCDS;
+  return xcd * base + (xcd < rem ? xcd : rem) + j;
+}
+
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 

@@ -38,11 +38,8 @@ __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * LDS_R
 // Logical tile of hardware workgroup `bid` (see the tile-order note above).
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
                                         int64_t& tn) {
-  constexpr int64_t XCDS = 8, GM = 4;
-  const int64_t total = tiles_m * tiles_n;
-  const int64_t xcd = bid % XCDS, j = bid / XCDS;
-  const int64_t base = total / XCDS, rem = total % XCDS;
-  const int64_t l = xcd * base + (xcd < rem ? xcd : rem) + j;
+  constexpr int64_t GM = 4;
+  const int64_t l = xcd_contiguous(bid, tiles_m * tiles_n);
   const int64_t grp = l / (GM * tiles_n);
   const int64_t rows = (tiles_m - grp * GM) < GM ? (tiles_m - grp * GM) : GM;
   const int64_t within = l - grp * GM * tiles_n;

@@ -1,0 +1,108 @@
+"""Parity at the full workload sizes (GPU), on 512 sampled query rows, plus the
+bit-identity sweep over chunk settings at full size.
+
+For each workload: the block runs through the C ABI for every chunk setting of
+its sweep, in the launch configuration ``bench.py`` times; the output bytes
+must be identical across the sweep ("LayerStream: H3 Chunking": chunked output
+is bit-identical). The oracle computes norm1 and K/V for all N tokens and the
+remaining steps for the sampled rows (exact for them). The attention output O
+is also recomputed through the step kernels for the sampled rows against all N
+keys and checked directly, because its contribution to y sits near the bf16
+resolution of y.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.dit_block as O
+from _helpers import check_bf16_bar, max_abs, oracle_inputs, rel_l2, to_f64
+from memory_bounded_chunked_amd import block as B
+from memory_bounded_chunked_amd import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+SWEEPS = {
+    "mid": [(4096, 4096, 0), (0, 16384, 0), (3000, 5000, 0)],
+    "large": [(8192, 8192, 0), (0, 32768, 0), (5000, 3000, 0)],
+    "longclip": [(8192, 8192, 3456), (16384, 4096, 3456)],
+    "int8": [(a, m, 0) for a in (0, 2048, 8192) for m in (2048, 8192)],
+}
+
+
+def _forward(blk, x0, mod, n, ca, cm, fc):
+    x = x0.clone()
+    ws = torch.empty(blk.peak_workspace(n, ca, cm, fc), dtype=torch.uint8, device="cuda")
+    blk.forward(x, mod, ca, cm, fc, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    return x
+
+
+def _gpu_attention_rows(shape, inputs, rows, x0, mod):
+    """O for the sampled rows through the step kernels: norm1 of all tokens, K and
+    V^T of all tokens, Q of the sampled rows, attention against all N keys."""
+    n, d = shape.n_tokens, shape.d
+    dt = shape.dtype
+    dev = "cuda"
+    w = {k: B.tensor_from_stored(v, dev) for k, v in inputs.items() if k[:2] in ("w_", "s_")}
+    n1 = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+    B.modnorm(x0, mod[0], mod[1], n1, eps=shape.eps)
+    sq = w.get("s_qkv")
+    kk = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+    B.linear(dt, "store", n1, w["w_qkv"][d:2 * d], kk, d, w_scale=None if sq is None else sq[d:2 * d])
+    ldv = (n + 63) // 64 * 64
+    vt = torch.empty(d, ldv, dtype=torch.bfloat16, device=dev)
+    B.linear(dt, "store_t", n1, w["w_qkv"][2 * d:], vt, d, w_scale=None if sq is None else sq[2 * d:])
+    idx = torch.from_numpy(rows).to(dev)
+    n1r = n1.index_select(0, idx).contiguous()
+    del n1
+    qr = torch.empty(len(rows), d, dtype=torch.bfloat16, device=dev)
+    B.linear(dt, "store", n1r, w["w_qkv"][:d], qr, d, w_scale=None if sq is None else sq[:d])
+    o = torch.empty(len(rows), d, dtype=torch.bfloat16, device=dev)
+    B.attention(qr, kk, vt, o, shape.n_heads, n_kv=n)
+    torch.cuda.synchronize()
+    return to_f64(o)
+
+
+@pytest.mark.parametrize("name", list(SWEEPS))
+def test_full_size_parity_and_bit_identity(name):
+    shape = synth.CONFIGS[name]
+    n = shape.n_tokens
+    inputs = synth.make_inputs(shape, seed=0)
+    blk, x0, mod = B.block_from_inputs(shape, inputs, "cuda")
+    digests = []
+    y_first = None
+    for ca, cm, fc in SWEEPS[name]:
+        y = _forward(blk, x0, mod, n, ca, cm, fc)
+        digests.append(hashlib.sha256(y.view(torch.uint8).cpu().numpy().tobytes()).hexdigest())
+        if y_first is None:
+            y_first = y.cpu()
+        del y
+    assert len(set(digests)) == 1, f"{name}: outputs differ across {SWEEPS[name]}"
+
+    rows = synth.sample_rows(n, 512)
+    o_gpu = _gpu_attention_rows(shape, inputs, rows, x0, mod)
+    blk.close()
+    del x0
+    torch.cuda.empty_cache()
+
+    x, modf, w = oracle_inputs(inputs)
+    y_ref, o_ref = O.block_rows(x, modf, w, shape.n_heads, rows, eps=shape.eps, want=("o",))
+    y = to_f64(y_first[torch.from_numpy(rows)])
+    o_rel = rel_l2(o_gpu, o_ref)
+    print(f"\n{name}: y max_abs={max_abs(y, y_ref):.4g} rel_l2={rel_l2(y, y_ref):.4g} "
+          f"max|y_ref|={np.abs(y_ref).max():.4g}; O rel_l2={o_rel:.4g}")
+    if shape.dtype == "w8_bf16":
+        # int8 weights (std ~0.045) push per-head logits to O(1e2): the bf16
+        # rounding of norm1, Q and K that bf16 activations require moves the
+        # softmax weights by tens of percent. An fp64 emulation of exactly this
+        # block's rounding points gives rel-L2 0.017 on y; the bar is 3e-2 on y
+        # (max-abs relative to max|y_ref|) and 5e-2 on O.
+        assert rel_l2(y, y_ref) <= 3e-2
+        assert max_abs(y, y_ref) <= 3e-2 * np.abs(y_ref).max()
+        assert o_rel <= 5e-2
+    else:
+        check_bf16_bar(y, y_ref)
+        assert o_rel <= 1e-2
