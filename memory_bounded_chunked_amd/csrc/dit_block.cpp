@@ -208,19 +208,27 @@ int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
     g.a = slab_a;
     g.lda = d;
     g.M = c;
-    g.N = d;
     g.K = d;
     g.ldb = d;
-    g.b = wqkv + d * d * wb;
+    g.b = wqkv + d * d * wb;  // K rows then V rows of w_qkv
     g.bscale = s_qkv ? s_qkv + d : nullptr;
     g.out = kbuf + s0 * d * e;
     g.ldo = d;
-    DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE, g, st));
-    g.b = wqkv + 2 * d * d * wb;
-    g.bscale = s_qkv ? s_qkv + 2 * d : nullptr;
-    g.out = vtbuf + s0 * e;
-    g.ldo = p.np;
-    DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
+    if (d % 256 == 0) {  // one launch: K row-major, V transposed
+      g.N = 2 * d;
+      g.out2 = vtbuf + s0 * e;
+      g.ldo2 = p.np;
+      g.split = d;
+      DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_KV, g, st));
+    } else {
+      g.N = d;
+      DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE, g, st));
+      g.b = wqkv + 2 * d * d * wb;
+      g.bscale = s_qkv ? s_qkv + 2 * d : nullptr;
+      g.out = vtbuf + s0 * e;
+      g.ldo = p.np;
+      DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
+    }
   }
 
   // ---- pass 2: super-slices of S tokens

@@ -266,33 +266,56 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
           }
         }
       }
-  } else if constexpr (EPI == EPI_STORE_T) {
+  } else if constexpr (EPI == EPI_STORE_T || EPI == EPI_KV) {
+    // transposed store: four consecutive rows of one column per 8-byte write
+    auto store_t = [&](TA* out, int64_t ldo, int64_t col_base) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NTL; ++j) {
-        const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-        const float sc = bscale ? bscale[col] : 1.f;
-        TA* orow = static_cast<TA*>(g.out) + col * g.ldo;
+        for (int j = 0; j < NTL; ++j) {
+          const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+          const float sc = bscale ? bscale[col] : 1.f;
+          TA* orow = out + (col - col_base) * ldo;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t row0 = m0 + wm * WTM + i * 32 + 8 * q + 4 * half;
-          float v[4];
+          for (int q = 0; q < 4; ++q) {
+            const int64_t row0 = m0 + wm * WTM + i * 32 + 8 * q + 4 * half;
+            float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * sc;
-          if (row0 + 3 < g.M) {
-            if constexpr (sizeof(TA) == 2) {
-              *reinterpret_cast<u32x2*>(orow + row0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * sc;
+            if (row0 + 3 < g.M) {
+              if constexpr (sizeof(TA) == 2) {
+                *reinterpret_cast<u32x2*>(orow + row0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              } else {
+                *reinterpret_cast<f32x4*>(orow + row0) = f32x4{v[0], v[1], v[2], v[3]};
+              }
             } else {
-              *reinterpret_cast<f32x4*>(orow + row0) = f32x4{v[0], v[1], v[2], v[3]};
-            }
-          } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (row0 + t < g.M) store_act(orow + row0 + t, v[t]);
+              for (int t = 0; t < 4; ++t)
+                if (row0 + t < g.M) store_act(orow + row0 + t, v[t]);
+            }
           }
         }
+    };
+    if constexpr (EPI == EPI_KV) {
+      if (tn * BN < g.split) {  // uniform per workgroup: the split is tile-aligned
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) {
+            const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+            const float sc = bscale ? bscale[col] : 1.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (row < g.M) store_act(static_cast<TA*>(g.out) + row * g.ldo + col, acc[i][j][r] * sc);
+            }
+          }
+      } else {
+        store_t(static_cast<TA*>(g.out2), g.ldo2, g.split);
       }
+    } else {
+      store_t(static_cast<TA*>(g.out), g.ldo, 0);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -361,6 +384,7 @@ static hipError_t launch_types(Epilogue epi, const GemmArgs& g, hipStream_t st) 
     case EPI_GATEUP: return launch_epi<TA, TB, EPI_GATEUP>(g, st);
     case EPI_ACCUM: return launch_epi<TA, TB, EPI_ACCUM>(g, st);
     case EPI_FINAL: return launch_epi<TA, TB, EPI_FINAL>(g, st);
+    case EPI_KV: return launch_epi<TA, TB, EPI_KV>(g, st);
   }
   return hipErrorInvalidValue;
 }

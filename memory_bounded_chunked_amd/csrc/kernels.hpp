@@ -18,6 +18,8 @@ enum Epilogue : int {
   EPI_GATEUP = 3,   // out[m][f] = silu(acc_gate) * acc_up    (B rows paired gate/up)
   EPI_ACCUM = 4,    // out[m][n] (fp32) += gate[n] * acc
   EPI_FINAL = 5,    // out[m][n] = aux[m][n] (fp32) + gate[n] * acc     out: activation type
+  EPI_KV = 6,       // columns [0, split): out[m][n] = acc; columns [split, N):
+                    // out2[n - split][m] = acc (K row-major and V transposed, one launch)
 };
 
 struct GemmArgs {
@@ -33,6 +35,9 @@ struct GemmArgs {
   const void* aux;      // RESID: x rows; FINAL: fp32 stage rows
   int64_t ldaux;
   const float* gate;    // RESID/ACCUM/FINAL: gate vector indexed by output column
+  void* out2;           // KV: transposed destination of the columns from `split` on
+  int64_t ldo2;
+  int64_t split;        // KV: first column stored transposed (a multiple of the tile width)
 };
 
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
