@@ -105,6 +105,25 @@ int dit_block_peak_workspace(const dit_block* h, int64_t n_tokens, int64_t attn_
                              int64_t mlp_chunk_tokens, int64_t ffn_chunk_features,
                              size_t* bytes_out);
 
+/* Automatic chunk sizing: the largest chunks whose workspace fits
+ * `budget_bytes` ("Proposal: Generic memory-aware streaming execution ...",
+ * section "Automatic chunk sizing": pick the largest chunks that fit a memory
+ * envelope; "LayerStream: H3 Chunking", "The two numbers you set": use the
+ * largest chunk that fits).
+ * Candidates use one token chunk C for both attention and MLP slices: all N
+ * tokens, or a multiple of 256 (the node's step) below N. The FFN width fc is
+ * F, F/2, F/4, ... while it stays a multiple of 64. The choice maximises C,
+ * and among equal C prefers the largest fc (no feature slicing when possible).
+ * Outputs: *attn_chunk_tokens (0 when C covers all N tokens),
+ * *mlp_chunk_tokens = C, *ffn_chunk_features (0 when fc = F); then
+ * dit_block_peak_workspace(h, n_tokens, ...) <= budget_bytes.
+ * Errors: DIT_EINVAL for a null pointer or n_tokens < 1; DIT_ENOSPC when not
+ * even C = 256 fits (global K/V alone is N*d*e + d*Np*e bytes: the floor
+ * that chunking cannot go below, "Where people get burned"). */
+int dit_block_plan_chunks(const dit_block* h, int64_t n_tokens, size_t budget_bytes,
+                          int64_t* attn_chunk_tokens, int64_t* mlp_chunk_tokens,
+                          int64_t* ffn_chunk_features);
+
 /* One block forward, in place.
  *   x          [N][d] activations (fp32 for F32, else bf16), read and
  *              overwritten with the block output y. 16-byte aligned.

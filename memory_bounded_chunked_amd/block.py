@@ -24,7 +24,7 @@ EPILOGUES = {"store": 0, "store_t": 1, "resid": 2, "gateup": 3, "accum": 4, "fin
 DEFAULT_ATTN_CHUNK = 8192
 DEFAULT_MLP_CHUNK = 8192
 
-EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_forward",
+EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
            "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention", "dit_linear",
            "dit_profile_enable", "dit_profile_read")
 PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down")
@@ -61,6 +61,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_block_create.restype = ctypes.c_int
     lib.dit_block_peak_workspace.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.dit_block_peak_workspace.restype = ctypes.c_int
+    lib.dit_block_plan_chunks.argtypes = [vp, i64, ctypes.c_size_t, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                          ctypes.POINTER(i64)]
+    lib.dit_block_plan_chunks.restype = ctypes.c_int
     lib.dit_block_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.dit_block_forward.restype = ctypes.c_int
     lib.dit_block_destroy.argtypes = [vp]
@@ -138,6 +141,14 @@ class DitBlock:
                                                   ffn_chunk_features, ctypes.byref(out)),
                "dit_block_peak_workspace")
         return out.value
+
+    def plan_chunks(self, n_tokens: int, budget_bytes: int) -> tuple:
+        """(attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features): the largest chunks
+        whose workspace fits ``budget_bytes`` (see ``dit_block_plan_chunks``)."""
+        a, m, f = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(self._lib.dit_block_plan_chunks(self._h, n_tokens, budget_bytes, ctypes.byref(a), ctypes.byref(m),
+                                               ctypes.byref(f)), "dit_block_plan_chunks")
+        return a.value, m.value, f.value
 
     def forward(self, x: torch.Tensor, mod: torch.Tensor, attn_chunk_tokens: int = DEFAULT_ATTN_CHUNK,
                 mlp_chunk_tokens: int = DEFAULT_MLP_CHUNK, ffn_chunk_features: int = 0,

@@ -161,6 +161,44 @@ int dit_block_peak_workspace(const dit_block* h, int64_t n_tokens, int64_t attn_
   return DIT_OK;
 }
 
+int dit_block_plan_chunks(const dit_block* h, int64_t n_tokens, size_t budget_bytes, int64_t* attn_chunk_tokens,
+                          int64_t* mlp_chunk_tokens, int64_t* ffn_chunk_features) {
+  if (!h || !attn_chunk_tokens || !mlp_chunk_tokens || !ffn_chunk_features || n_tokens < 1) return DIT_EINVAL;
+  const int64_t f = h->desc.ffn;
+  auto fits = [&](int64_t c, int64_t fc) {
+    Plan p;
+    return make_plan(h, n_tokens, c, c, fc == f ? 0 : fc, &p) == DIT_OK && p.total <= budget_bytes;
+  };
+  int64_t best_c = 0, best_fc = 0;
+  for (int64_t fc = f; fc >= 64 && fc % 64 == 0; fc = (fc % 128 == 0) ? fc / 2 : 0) {
+    int64_t c = 0;
+    if (fits(n_tokens, fc)) {
+      c = n_tokens;
+    } else {
+      // workspace grows with C, so the largest fitting multiple of 256 is found by bisection
+      int64_t lo = 0, hi = (n_tokens - 1) / 256;  // in units of 256 tokens
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (fits(mid * 256, fc))
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      c = lo * 256;
+    }
+    if (c > best_c) {
+      best_c = c;
+      best_fc = fc;
+    }
+    if (best_c == n_tokens) break;
+  }
+  if (best_c == 0) return DIT_ENOSPC;
+  *attn_chunk_tokens = best_c >= n_tokens ? 0 : best_c;
+  *mlp_chunk_tokens = best_c;
+  *ffn_chunk_features = best_fc == f ? 0 : best_fc;
+  return DIT_OK;
+}
+
 int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens, int64_t attn_chunk_tokens,
                       int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
                       size_t workspace_bytes, void* stream) {

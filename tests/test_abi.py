@@ -156,3 +156,52 @@ def test_defaults_follow_the_pages():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "chunk_knobs.json")))
     assert B.DEFAULT_ATTN_CHUNK == g["attn_chunk_tokens"]["default"]
     assert B.DEFAULT_MLP_CHUNK == g["mlp_chunk_tokens"]["default"]
+
+
+def _plan(lib, h, n, budget):
+    a, m, f = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.dit_block_plan_chunks(h, n, budget, ctypes.byref(a), ctypes.byref(m), ctypes.byref(f))
+    return rc, a.value, m.value, f.value
+
+
+@pytest.mark.parametrize("n,dtype", [(32768, 1), (131072, 1), (65536, 2), (1000, 0)])
+def test_plan_chunks_fits_and_is_maximal(lib, n, dtype):
+    d, ffn = (256, 1024) if n == 1000 else (5120, 13824)
+    rc, h = _handle(lib, d=d, heads=d // 128, ffn=ffn, dtype=dtype)
+    assert rc == 0
+    e = 4 if dtype == 0 else 2
+    kv = _closed_form(n, d, ffn, e, n, 1, 64) - (n * d * 4) - max(2 * n * d * e, d * e + 64 * e)
+    for extra_mib in (1, 64, 300, 1200, 4000, 100000):
+        budget = kv + extra_mib * 2 ** 20
+        rc, ca, cm, fc = _plan(lib, h, n, budget)
+        if rc == B.DIT_ENOSPC:
+            # not even a 256-token chunk at the narrowest candidate feature width fits
+            fc_min = ffn
+            while fc_min % 128 == 0 and (fc_min // 2) % 64 == 0:
+                fc_min //= 2
+            assert _ws(lib, h, n, min(256, n), min(256, n), fc_min)[1] > budget
+            continue
+        assert rc == 0
+        c = n if ca == 0 else ca
+        assert cm == c and (c == n or c % 256 == 0)
+        rc, ws = _ws(lib, h, n, ca, cm, fc)
+        assert rc == 0 and ws <= budget
+        if c < n:  # one more step of 256 tokens does not fit at any candidate feature width
+            for f2 in (0, ffn // 2, ffn // 4, ffn // 8):
+                if f2 and f2 % 64:
+                    continue
+                nxt = min(n, c + 256)
+                assert _ws(lib, h, n, 0 if nxt == n else nxt, nxt, f2)[1] > budget
+    # a budget below the global K/V floor is refused
+    assert _plan(lib, h, n, kv // 2)[0] == B.DIT_ENOSPC
+    # ample memory: one slice of all tokens, no feature slicing
+    assert _plan(lib, h, n, 1 << 50)[1:] == (0, n, 0)
+    lib.dit_block_destroy(h)
+
+
+def test_plan_chunks_rejects(lib):
+    rc, h = _handle(lib)
+    a = ctypes.c_int64()
+    assert lib.dit_block_plan_chunks(h, 0, 1 << 30, ctypes.byref(a), ctypes.byref(a), ctypes.byref(a)) == B.DIT_EINVAL
+    assert lib.dit_block_plan_chunks(None, 10, 1 << 30, ctypes.byref(a), ctypes.byref(a), ctypes.byref(a)) == B.DIT_EINVAL
+    lib.dit_block_destroy(h)

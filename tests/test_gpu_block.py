@@ -135,3 +135,23 @@ def test_closed_forms_on_device():
     x, mod, w = oracle_inputs(inp1)
     y1 = to_f64(run_block(one, inp1, 0, 1))
     check_bf16_bar(y1, O.block_forward(x, mod, w, one.n_heads))
+
+
+def test_planned_chunks_run_within_budget():
+    shape = SMALL["bf16"]
+    inputs = synth.make_inputs(shape, 0)
+    x, mod, w = oracle_inputs(inputs)
+    y_ref = O.block_forward(x, mod, w, shape.n_heads)
+    blk, xt, modt = B.block_from_inputs(shape, inputs, "cuda")
+    n = shape.n_tokens
+    floor = blk.peak_workspace(n, 256, 256, 64) - 256 * shape.d * 4 - max(2 * 256 * shape.d * 2,
+                                                                          256 * shape.d * 2 + 256 * 64 * 2)
+    for extra in (200_000, 700_000, 10 ** 9):
+        ca, cm, fc = blk.plan_chunks(n, floor + extra)
+        need = blk.peak_workspace(n, ca, cm, fc)
+        assert need <= floor + extra
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        xx = xt.clone()
+        blk.forward(xx, modt, ca, cm, fc, workspace=ws)
+        torch.cuda.synchronize()
+        check_bf16_bar(to_f64(xx), y_ref)
