@@ -25,8 +25,8 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-__all__ = ["BlockShape", "CONFIGS", "make_inputs", "bf16_bits_to_f64",
-           "f64_to_bf16_bits", "sample_rows", "to_f64"]
+__all__ = ["BlockShape", "CONFIGS", "make_inputs", "make_qk_inputs", "rope_tables",
+           "bf16_bits_to_f64", "f64_to_bf16_bits", "sample_rows", "to_f64"]
 
 _BLOCK_ELEMS = 1 << 23  # values per draw call when filling large arrays
 
@@ -138,6 +138,27 @@ def make_inputs(shape: BlockShape, seed: int = 0, with_x: bool = True) -> dict:
         else:
             out["w_" + name] = _normal(rng, wshape, wstd, act)
     return out
+
+
+def rope_tables(n_tokens: int, head_dim: int, base: float = 10000.0, offset: int = 0):
+    """fp32 cos/sin tables [N, head_dim/2] for 1-D token positions offset..offset+N-1:
+    angle(i, j) = (offset + i) * base^(-2j / head_dim), drawn in fp64, rounded once."""
+    pos = np.arange(offset, offset + n_tokens, dtype=np.float64)[:, None]
+    freq = base ** (-2.0 * np.arange(head_dim // 2, dtype=np.float64) / head_dim)
+    ang = pos * freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_qk_inputs(shape: BlockShape, seed: int = 0) -> dict:
+    """Optional QK-norm weights and RoPE tables for ``shape``: ``q_norm`` and
+    ``k_norm`` [head_dim] fp32 ~ 1 + N(0, variance 0.01), drawn from
+    PCG64(seed + 1000) (so the block's own draws are unchanged), and ``cos`` /
+    ``sin`` from ``rope_tables``."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    q_norm = (1.0 + 0.1 * rng.standard_normal(shape.head_dim)).astype(np.float32)
+    k_norm = (1.0 + 0.1 * rng.standard_normal(shape.head_dim)).astype(np.float32)
+    cos, sin = rope_tables(shape.n_tokens, shape.head_dim)
+    return {"q_norm": q_norm, "k_norm": k_norm, "cos": cos, "sin": sin}
 
 
 def to_f64(arr: np.ndarray) -> np.ndarray:

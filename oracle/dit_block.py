@@ -32,6 +32,7 @@ import numpy as np
 
 __all__ = [
     "layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
+    "rms_norm_heads", "rope", "qk_transform",
     "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
 ]
 
@@ -101,6 +102,48 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int) -> np.n
     return out
 
 
+def rms_norm_heads(t: np.ndarray, w: np.ndarray, n_heads: int, eps: float) -> np.ndarray:
+    """Per token and head: t_h / sqrt(mean(t_h^2) + eps) * w, w of length dh.
+
+    The optional Q/K normalization step of the streamed-Q plan (streaming
+    proposal, "Attention requires a stronger contract": apply the model's Q
+    normalization/positional transform to each bounded Q region).
+    """
+    n, d = t.shape
+    dh = d // n_heads
+    th = t.reshape(n, n_heads, dh)
+    ms = (th ** 2).mean(axis=2, keepdims=True)
+    return (th / np.sqrt(ms + eps) * np.asarray(w, np.float64)).reshape(n, d)
+
+
+def rope(t: np.ndarray, cos: np.ndarray, sin: np.ndarray, n_heads: int) -> np.ndarray:
+    """Rotary positional transform on adjacent pairs of every head.
+
+    For token i and pair j of a head: (a, b) = (t[2j], t[2j+1]) becomes
+    (a cos_ij - b sin_ij, a sin_ij + b cos_ij); ``cos``/``sin`` are [N, dh/2],
+    shared by all heads (the "positional encoding/RoPE step" of the same plan).
+    """
+    n, d = t.shape
+    dh = d // n_heads
+    th = t.reshape(n, n_heads, dh // 2, 2)
+    a, b = th[..., 0], th[..., 1]
+    c = np.asarray(cos, np.float64)[:, None, :]
+    s = np.asarray(sin, np.float64)[:, None, :]
+    out = np.empty_like(th)
+    out[..., 0] = a * c - b * s
+    out[..., 1] = a * s + b * c
+    return out.reshape(n, d)
+
+
+def qk_transform(t: np.ndarray, norm_w, cos, sin, n_heads: int, eps: float) -> np.ndarray:
+    """RMSNorm (if a weight is given), then RoPE (if tables are given)."""
+    if norm_w is not None:
+        t = rms_norm_heads(t, norm_w, n_heads, eps)
+    if cos is not None:
+        t = rope(t, cos, sin, n_heads)
+    return t
+
+
 def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """Weight-only int8: W[n, k] = s[n] * q[n, k], one scale per output row.
 
@@ -137,14 +180,16 @@ def _mlp_delta(n2: np.ndarray, w: dict, ffn: int, f0: int = 0, f1: int | None = 
 
 
 def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
-                  eps: float = 1e-6, want: tuple = ()) -> np.ndarray | tuple:
+                  eps: float = 1e-6, want: tuple = (), qk: dict | None = None) -> np.ndarray | tuple:
     """Unchunked block forward; returns y [N, d] (and the named intermediates).
 
     n1 = modulate(LN(x); shift1, scale1);  q, k, v = n1 W_{q,k,v}^T
     o  = attention(q, k, v);               x1 = x + gate1 * (o W_o^T)
     n2 = modulate(LN(x1); shift2, scale2); h = silu(n2 W_g^T) * (n2 W_u^T)
     y  = x1 + gate2 * (h W_down^T)
-    ``want`` may name any of n1, q, k, v, o, x1, n2, h.
+    ``want`` may name any of n1, q, k, v, o, x1, n2, h. ``qk`` optionally holds
+    ``q_norm`` / ``k_norm`` ([dh] RMSNorm weights) and ``cos`` / ``sin``
+    ([N, dh/2] RoPE tables), applied to q and k before attention.
     """
     d = x.shape[1]
     ffn = w["down"].shape[1]
@@ -152,6 +197,9 @@ def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
     wq, wk, wv = _split(w, d)
     n1 = modulate(layer_norm(x, eps), sh1, sc1)
     q, k, v = linear(n1, wq), linear(n1, wk), linear(n1, wv)
+    if qk:
+        q = qk_transform(q, qk.get("q_norm"), qk.get("cos"), qk.get("sin"), n_heads, eps)
+        k = qk_transform(k, qk.get("k_norm"), qk.get("cos"), qk.get("sin"), n_heads, eps)
     o = attention(q, k, v, n_heads)
     x1 = x + g1 * linear(o, w["o"])
     n2 = modulate(layer_norm(x1, eps), sh2, sc2)
@@ -167,7 +215,7 @@ def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
 
 def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
                           attn_chunk: int, mlp_chunk: int, ffn_chunk: int = 0,
-                          eps: float = 1e-6) -> np.ndarray:
+                          eps: float = 1e-6, qk: dict | None = None) -> np.ndarray:
     """The pages' two-pass, token-chunked schedule of the same block, in place.
 
     Follows "How the slicing works" (LayerStream: H3 Chunking) and "Attention
@@ -195,15 +243,23 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
 
     k = np.empty((n, d))
     v = np.empty((n, d))
+    qk = qk or {}
+    cos, sin = qk.get("cos"), qk.get("sin")
+
+    def rows(tab, a, b):
+        return None if tab is None else tab[a:b]
+
     for s0 in range(0, n, ca):                      # pass 1: K and V only
         s1 = min(n, s0 + ca)
         n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
-        k[s0:s1] = linear(n1, wk)
+        k[s0:s1] = qk_transform(linear(n1, wk), qk.get("k_norm"), rows(cos, s0, s1), rows(sin, s0, s1),
+                                n_heads, eps)
         v[s0:s1] = linear(n1, wv)
     for s0 in range(0, n, ca):                      # pass 2: Q slice vs global K/V
         s1 = min(n, s0 + ca)
         n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
-        o = attention(linear(n1, wq), k, v, n_heads)
+        q = qk_transform(linear(n1, wq), qk.get("q_norm"), rows(cos, s0, s1), rows(sin, s0, s1), n_heads, eps)
+        o = attention(q, k, v, n_heads)
         res[s0:s1] += g1 * linear(o, w["o"])
     for m0 in range(0, n, cm):                      # MLP, token slabs
         m1 = min(n, m0 + cm)
@@ -216,7 +272,7 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
 
 
 def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.ndarray,
-               eps: float = 1e-6, want: tuple = ()) -> np.ndarray | tuple:
+               eps: float = 1e-6, want: tuple = (), qk: dict | None = None) -> np.ndarray | tuple:
     """The block output for the query rows ``rows`` only (exact for those rows).
 
     norm1 and K/V are computed for all N tokens, because every query attends
@@ -226,12 +282,16 @@ def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.n
     ffn = w["down"].shape[1]
     sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
     wq, wk, wv = _split(w, d)
+    qk = qk or {}
+    cos, sin = qk.get("cos"), qk.get("sin")
     n1_all = modulate(layer_norm(x, eps), sh1, sc1)
     k, v = linear(n1_all, wk), linear(n1_all, wv)
     del n1_all
+    k = qk_transform(k, qk.get("k_norm"), cos, sin, n_heads, eps)
     xr = x[rows]
     n1 = modulate(layer_norm(xr, eps), sh1, sc1)
-    q = linear(n1, wq)
+    q = qk_transform(linear(n1, wq), qk.get("q_norm"), None if cos is None else cos[rows],
+                     None if sin is None else sin[rows], n_heads, eps)
     o = attention(q, k, v, n_heads)
     x1 = xr + g1 * linear(o, w["o"])
     n2 = modulate(layer_norm(x1, eps), sh2, sc2)

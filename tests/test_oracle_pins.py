@@ -216,8 +216,86 @@ def pin_rows(M):
     assert _rel(yr, y[rows]) < 1e-12 and _rel(orow, o[rows]) < 1e-12 and _rel(x1r, x1[rows]) < 1e-12
 
 
+def _qk_case(n=23, d=32, heads=2, ffn=64, seed=3):
+    x, mod, w, heads = _case(d=d, heads=heads, ffn=ffn, n=n, seed=seed)
+    sh = synth.BlockShape("t", d, heads, d // heads, ffn, n, "bf16")
+    qk = {k: np.asarray(v, np.float64) for k, v in synth.make_qk_inputs(sh, seed).items()}
+    return x, mod, w, heads, qk
+
+
+def pin_rms_norm_heads(M):
+    rng = np.random.default_rng(11)
+    t = rng.standard_normal((9, 3 * 16)) * 2.5
+    wv = 1.0 + 0.3 * rng.standard_normal(16)
+    got = M.rms_norm_heads(t, wv, 3, 1e-6)
+    ref = tF.rms_norm(torch.from_numpy(t).reshape(9, 3, 16), (16,), torch.from_numpy(wv), eps=1e-6)
+    assert _rel(got, ref.reshape(9, 48).numpy()) < 1e-12, "rms_norm vs torch"
+    unit = M.rms_norm_heads(t, np.ones(16), 3, 0.0).reshape(9, 3, 16)
+    assert np.abs(np.sqrt((unit ** 2).mean(axis=2)) - 1).max() < 1e-12, "unit RMS per head"
+
+
+def pin_rope(M):
+    rng = np.random.default_rng(12)
+    n, heads, dh = 7, 2, 8
+    t = rng.standard_normal((n, heads * dh))
+    ang = rng.uniform(-4, 4, (n, dh // 2))
+    got = M.rope(t, np.cos(ang), np.sin(ang), heads)
+    # the same rotation as a complex product (a + ib) e^{i angle}
+    z = t.reshape(n, heads, dh // 2, 2)
+    zc = (z[..., 0] + 1j * z[..., 1]) * np.exp(1j * ang)[:, None, :]
+    ref = np.stack([zc.real, zc.imag], axis=-1).reshape(n, heads * dh)
+    assert _rel(got, ref) < 1e-12, "rope vs complex rotation"
+    assert np.array_equal(M.rope(t, np.ones((n, dh // 2)), np.zeros((n, dh // 2)), heads), t), "zero angle"
+    # scores depend only on the position difference
+    cos_a, sin_a = synth.rope_tables(n, dh, offset=0)
+    cos_b, sin_b = synth.rope_tables(n, dh, offset=37)
+    q, k = rng.standard_normal((n, heads * dh)), rng.standard_normal((n, heads * dh))
+    sa = M.rope(q, cos_a, sin_a, heads) @ M.rope(k, cos_a, sin_a, heads).T
+    sb = M.rope(q, cos_b, sin_b, heads) @ M.rope(k, cos_b, sin_b, heads).T
+    assert np.abs(sa - sb).max() < 1e-5, "relative positions"  # tables are fp32
+
+
+def pin_block_qk(M):
+    x, mod, w, heads, qk = _qk_case()
+    n, d = x.shape
+    dh = d // heads
+    X = torch.from_numpy(x)
+    sh1, sc1 = torch.from_numpy(mod[0]), torch.from_numpy(mod[1])
+    n1 = tF.layer_norm(X, (d,), eps=1e-6) * (1 + sc1) + sh1
+    q, k, v = tF.linear(n1, torch.from_numpy(w["qkv"])).split(d, dim=1)
+
+    def norm_rope(t, wv):
+        th = tF.rms_norm(t.reshape(n, heads, dh), (dh,), torch.from_numpy(wv), eps=1e-6)
+        zc = torch.view_as_complex(th.reshape(n, heads, dh // 2, 2).contiguous())
+        rot = torch.polar(torch.ones(n, dh // 2, dtype=torch.float64),
+                          torch.atan2(torch.from_numpy(qk["sin"]), torch.from_numpy(qk["cos"])))
+        return torch.view_as_real(zc * rot[:, None, :]).reshape(n, d)
+
+    q, k = norm_rope(q, qk["q_norm"]), norm_rope(k, qk["k_norm"])
+
+    def hd(t):
+        return t.reshape(n, heads, dh).transpose(0, 1).unsqueeze(0)
+
+    o = tF.scaled_dot_product_attention(hd(q), hd(k), hd(v)).squeeze(0).transpose(0, 1).reshape(n, d)
+    _, o_or = M.block_forward(x, mod, w, heads, want=("o",), qk=qk)
+    # the fp32 tables are not exactly unit-norm pairs, so compare at the tables' precision
+    assert _rel(o_or, o.numpy()) < 1e-6, "qk-norm + rope block vs torch"
+    y = M.block_forward(x, mod, w, heads, qk=qk)
+    rows = np.array([0, 5, n - 1])
+    assert _rel(M.block_rows(x, mod, w, heads, rows, qk=qk), y[rows]) < 1e-12, "rows with qk"
+    saved = M.matmul
+    try:
+        M.matmul = _order_stable
+        y = M.block_forward(x, mod, w, heads, qk=qk)
+        for ca, cm in ((5, 7), (0, n), (22, 3)):
+            assert np.array_equal(M.block_forward_chunked(x, mod, w, heads, ca, cm, qk=qk), y), "chunked qk"
+    finally:
+        M.matmul = saved
+
+
 PINS = [pin_layer_norm, pin_silu, pin_attention_brute, pin_attention_sdpa, pin_block_torch,
-        pin_chunked_schedule, pin_closed_forms, pin_int8_rows, pin_rows]
+        pin_chunked_schedule, pin_closed_forms, pin_int8_rows, pin_rows, pin_rms_norm_heads, pin_rope,
+        pin_block_qk]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -230,7 +308,32 @@ def test_pin_holds(pin):
 
 _orig = {name: getattr(O, name) for name in
          ("layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
-          "block_forward", "block_forward_chunked")}
+          "block_forward", "block_forward_chunked", "rms_norm_heads", "rope", "qk_transform")}
+
+
+def _rope_sin_flipped(t, cos, sin, n_heads):
+    return _orig["rope"](t, cos, -np.asarray(sin), n_heads)
+
+
+def _rope_halves(t, cos, sin, n_heads):
+    # rotate (x_j, x_{j+dh/2}) instead of adjacent pairs
+    n, d = t.shape
+    dh = d // n_heads
+    th = t.reshape(n, n_heads, 2, dh // 2).transpose(0, 1, 3, 2).reshape(n, d)
+    return _orig["rope"](th, cos, sin, n_heads)
+
+
+def _rms_over_d(t, w, n_heads, eps):
+    ms = (t ** 2).mean(axis=1, keepdims=True)
+    return t / np.sqrt(ms + eps) * np.tile(np.asarray(w, np.float64), n_heads)
+
+
+def _qk_rope_first(t, norm_w, cos, sin, n_heads, eps):
+    if cos is not None:
+        t = _orig["rope"](t, cos, sin, n_heads)
+    if norm_w is not None:
+        t = _orig["rms_norm_heads"](t, norm_w, n_heads, eps)
+    return t
 
 
 def _ln_unbiased(x, eps):
@@ -328,6 +431,10 @@ MUTANTS = {
     "block: square out-projection transposed": ("block_forward", _block_wo_transposed),
     "block: MLP residual from x, not x1": ("block_forward", _block_mlp_residual_from_x),
     "chunked: K/V interleaved with in-place writes": ("block_forward_chunked", _chunked_interleaved),
+    "rope: sine sign flipped": ("rope", _rope_sin_flipped),
+    "rope: halves instead of adjacent pairs": ("rope", _rope_halves),
+    "qk-norm: RMS over all of d": ("rms_norm_heads", _rms_over_d),
+    "qk: rope before the norm": ("qk_transform", _qk_rope_first),
 }
 
 
