@@ -96,6 +96,7 @@ def main() -> int:
     ap.add_argument("--ffn-chunk", type=int, default=None)
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qk", action="store_true", help="with QK RMSNorm and RoPE (a widening of the path)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the block path is "
@@ -115,6 +116,11 @@ def main() -> int:
     t0 = time.perf_counter()
     inputs = synth.make_inputs(shape, seed=0)
     log(f"[bench] inputs for {shape.name} drawn in {time.perf_counter() - t0:.1f}s")
+    rope = None
+    if args.qk:
+        qk_in = synth.make_qk_inputs(shape, 0)
+        inputs = {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]}
+        rope = (torch.from_numpy(qk_in["cos"]).to(dev), torch.from_numpy(qk_in["sin"]).to(dev))
     blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
     x = x0.clone()
     ws_bytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
@@ -123,7 +129,7 @@ def main() -> int:
 
     def step():
         x.copy_(x0)
-        blk.forward(x, mod, ca, cm, fc, workspace=ws, stream=stream)
+        blk.forward(x, mod, ca, cm, fc, workspace=ws, stream=stream, rope=rope)
 
     for _ in range(args.warmup):
         step()
@@ -170,7 +176,8 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(att_tflops / peak, 4) if att_tflops else None,
-        "traffic": measured_traffic() if args.config == "large" and (ca, cm, fc) == (8192, 8192, 0) else None,
+        "traffic": (measured_traffic() if args.config == "large" and (ca, cm, fc) == (8192, 8192, 0)
+                    and not args.qk else None),
         "avg_launch_ms": round(att_avg_ms, 4) if att_avg_ms else None,
         "flops_per_launch": att_flops_launch,
     }
@@ -189,7 +196,8 @@ def main() -> int:
         "data": "synthetic (seeded PCG64 inputs; see DESIGN.md recipe)",
         "config": {
             "workload": (f"{shape.name} DiT block forward: d={d}, {shape.n_heads}x{shape.head_dim} heads, "
-                         f"SwiGLU F={shape.ffn}, N={n} tokens, batch 1"),
+                         f"SwiGLU F={shape.ffn}, N={n} tokens, batch 1"
+                         + (", QK RMSNorm + RoPE" if args.qk else "")),
             "n_tokens": n, "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
             "peak_workspace_bytes": ws_bytes,
             "tflops": round(tflops, 1),

@@ -80,6 +80,13 @@ typedef struct dit_block_weights {
   const float* s_o;    /* [d] */
   const float* s_gu;   /* [2F] */
   const float* s_down; /* [d] */
+  /* Optional QK RMSNorm weights, fp32 [head_dim], shared by all heads (NULL =
+   * no normalization): per token and head, t <- t / sqrt(mean(t^2) + eps) * w,
+   * applied to Q and K after their projection ("Proposal: Generic
+   * memory-aware streaming execution ...", "Attention requires a stronger
+   * contract": the model's Q normalization inside the streamed-Q plan). */
+  const float* q_norm;
+  const float* k_norm;
 } dit_block_weights;
 
 /* Validate the descriptor and weight pointers and create a handle that holds
@@ -148,6 +155,18 @@ int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
                       int64_t attn_chunk_tokens, int64_t mlp_chunk_tokens,
                       int64_t ffn_chunk_features, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* dit_block_forward with a rotary positional transform of Q and K: for token
+ * i and head pair j, (t[2j], t[2j+1]) <- (a cos - b sin, a sin + b cos) with
+ * cos = rope_cos[i][j], sin = rope_sin[i][j] (device, fp32 [N][head_dim/2],
+ * 16-byte aligned, read-only), applied after the QK normalization if any (the
+ * "positional encoding/RoPE step" of the same plan). Tables may be NULL
+ * together (then this equals dit_block_forward); one NULL alone is
+ * DIT_EINVAL. Other arguments, errors and guarantees as dit_block_forward. */
+int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float* rope_cos,
+                           const float* rope_sin, int64_t n_tokens, int64_t attn_chunk_tokens,
+                           int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Release the handle (host memory only; the weights stay the caller's). */
 void dit_block_destroy(dit_block* h);

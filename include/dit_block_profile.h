@@ -27,7 +27,8 @@ extern "C" {
 #define DIT_K_OUT_PROJ 4   /* out-projection + gated residual into fp32 staging */
 #define DIT_K_GATE_UP 5    /* SwiGLU gate/up projection of an MLP slab */
 #define DIT_K_DOWN 6       /* down projection + gated residual, in place */
-#define DIT_K_COUNT 7
+#define DIT_K_QK 7         /* optional QK RMSNorm / RoPE of a Q or K slab */
+#define DIT_K_COUNT 8
 
 /* on != 0: clear all records and start recording; on == 0: stop recording
  * (records are kept for dit_profile_read). Returns DIT_OK. */

@@ -47,6 +47,19 @@ int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int6
                   const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv,
                   int64_t n_heads, int64_t head_dim, void* stream);
 
+/* QK RMSNorm and/or RoPE in place on `rows` token rows (the Q normalization /
+ * positional transform of the streamed-Q plan, "Attention requires a stronger
+ * contract" of the streaming proposal):
+ *   norm_w != NULL: per head, t <- t / sqrt(mean(t^2) + eps) * norm_w  ([head_dim] fp32)
+ *   rope_cos/sin != NULL: per head pair j of row i, (a, b) <- (a c - b s, a s + b c),
+ *     c = rope_cos[i*ld_rope + j], s = rope_sin[i*ld_rope + j]
+ * x: [rows][ldx] of dtype DIT_F32 or DIT_BF16, d = n_heads*head_dim;
+ * head_dim 64 or 128; d <= 8192; ldx >= d, multiple of 8; ld_rope >=
+ * head_dim/2, multiple of 4; rope tables both or neither. */
+int dit_qk_transform(int32_t dtype, void* x, int64_t ldx, int64_t rows, int64_t n_heads, int64_t head_dim,
+                     const float* norm_w, const float* rope_cos, const float* rope_sin, int64_t ld_rope,
+                     float eps, void* stream);
+
 /* Epilogues of dit_linear (acc = sum_k a[m][k] * w[n][k] * s[n]). */
 #define DIT_EPI_STORE 0    /* out[m][n] = acc (activation type) */
 #define DIT_EPI_STORE_T 1  /* out[n][m] = acc (transposed store, used for V) */

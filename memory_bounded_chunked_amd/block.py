@@ -25,9 +25,9 @@ DEFAULT_ATTN_CHUNK = 8192
 DEFAULT_MLP_CHUNK = 8192
 
 EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
-           "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention", "dit_linear",
-           "dit_profile_enable", "dit_profile_read")
-PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down")
+           "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
+           "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read")
+PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk")
 
 
 class DitError(RuntimeError):
@@ -44,7 +44,8 @@ class _Desc(ctypes.Structure):
 class _Weights(ctypes.Structure):
     _fields_ = [("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("w_gu", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_qkv", ctypes.c_void_p), ("s_o", ctypes.c_void_p),
-                ("s_gu", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gu", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("q_norm", ctypes.c_void_p),
+                ("k_norm", ctypes.c_void_p)]
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -66,6 +67,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_block_plan_chunks.restype = ctypes.c_int
     lib.dit_block_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.dit_block_forward.restype = ctypes.c_int
+    lib.dit_block_forward_rope.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.dit_block_forward_rope.restype = ctypes.c_int
+    lib.dit_qk_transform.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, vp, i64, ctypes.c_float, vp]
+    lib.dit_qk_transform.restype = ctypes.c_int
     lib.dit_block_destroy.argtypes = [vp]
     lib.dit_block_destroy.restype = None
     lib.dit_block_strerror.argtypes = [ctypes.c_int]
@@ -120,7 +125,7 @@ class DitBlock:
         self._weights = dict(weights)
         desc = _Desc(d, n_heads, head_dim, ffn, DTYPES[dtype], eps)
         w = _Weights(*(_ptr(self._weights.get(k)) for k in
-                       ("w_qkv", "w_o", "w_gu", "w_down", "s_qkv", "s_o", "s_gu", "s_down")))
+                       ("w_qkv", "w_o", "w_gu", "w_down", "s_qkv", "s_o", "s_gu", "s_down", "q_norm", "k_norm")))
         h = ctypes.c_void_p()
         _check(self._lib.dit_block_create(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(h)),
                "dit_block_create")
@@ -152,16 +157,19 @@ class DitBlock:
 
     def forward(self, x: torch.Tensor, mod: torch.Tensor, attn_chunk_tokens: int = DEFAULT_ATTN_CHUNK,
                 mlp_chunk_tokens: int = DEFAULT_MLP_CHUNK, ffn_chunk_features: int = 0,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """Run the block in place on ``x`` [N, d]; returns ``x``."""
+                workspace: torch.Tensor | None = None, stream=None, rope: tuple | None = None) -> torch.Tensor:
+        """Run the block in place on ``x`` [N, d]; returns ``x``. ``rope`` = (cos, sin)
+        fp32 [N, head_dim/2] device tables for the rotary transform of Q and K."""
         n = x.shape[0]
         if workspace is None:
             nbytes = self.peak_workspace(n, attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features)
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-        _check(self._lib.dit_block_forward(self._h, x.data_ptr(), mod.data_ptr(), n, attn_chunk_tokens,
-                                           mlp_chunk_tokens, ffn_chunk_features, workspace.data_ptr(),
-                                           workspace.numel() * workspace.element_size(), _stream(stream)),
-               "dit_block_forward")
+        cs, sn = (None, None) if rope is None else rope
+        _check(self._lib.dit_block_forward_rope(self._h, x.data_ptr(), mod.data_ptr(), _ptr(cs), _ptr(sn), n,
+                                                attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features,
+                                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                                _stream(stream)),
+               "dit_block_forward_rope")
         return x
 
 
@@ -174,6 +182,18 @@ def modnorm(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, out: torc
                            scale.data_ptr(), out.data_ptr(), out.stride(0), x.shape[0], x.shape[1], eps,
                            _stream(stream)), "dit_modnorm")
     return out
+
+
+def qk_transform(x: torch.Tensor, n_heads: int, norm_w: torch.Tensor | None = None, rope: tuple | None = None,
+                 eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """QK RMSNorm and/or RoPE in place on the rows of ``x`` (one kernel)."""
+    lib = load_library()
+    dt = {torch.float32: 0, torch.bfloat16: 1}[x.dtype]
+    cs, sn = (None, None) if rope is None else rope
+    _check(lib.dit_qk_transform(dt, x.data_ptr(), x.stride(0), x.shape[0], n_heads, x.shape[1] // n_heads,
+                                _ptr(norm_w), _ptr(cs), _ptr(sn), 0 if cs is None else cs.stride(0), eps,
+                                _stream(stream)), "dit_qk_transform")
+    return x
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, n_heads: int,
@@ -230,7 +250,8 @@ def tensor_from_stored(arr, device) -> torch.Tensor:
 
 def block_from_inputs(shape, inputs: dict, device="cuda") -> tuple:
     """(DitBlock, x, mod) on ``device`` from a ``synth.BlockShape`` and its inputs."""
-    w = {k: tensor_from_stored(v, device) for k, v in inputs.items() if k[:2] in ("w_", "s_")}
+    w = {k: tensor_from_stored(v, device) for k, v in inputs.items()
+         if k[:2] in ("w_", "s_") or k in ("q_norm", "k_norm")}
     blk = DitBlock(shape.d, shape.n_heads, shape.head_dim, shape.ffn, shape.dtype, w, shape.eps)
     x = tensor_from_stored(inputs["x"], device) if "x" in inputs else None
     mod = tensor_from_stored(inputs["mod"], device)

@@ -141,6 +141,7 @@ int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit
   if (d.dtype == DIT_W8_BF16) {
     if (!w->s_qkv || !w->s_o || !w->s_gu || !w->s_down) return DIT_EINVAL;
   }
+  if ((w->q_norm && !aligned16(w->q_norm)) || (w->k_norm && !aligned16(w->k_norm))) return DIT_EINVAL;
   dit_block* h = new (std::nothrow) dit_block;
   if (!h) return DIT_EINVAL;
   h->desc = d;
@@ -202,11 +203,20 @@ int dit_block_plan_chunks(const dit_block* h, int64_t n_tokens, size_t budget_by
 int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens, int64_t attn_chunk_tokens,
                       int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
                       size_t workspace_bytes, void* stream) {
+  return dit_block_forward_rope(h, x, mod, nullptr, nullptr, n_tokens, attn_chunk_tokens, mlp_chunk_tokens,
+                                ffn_chunk_features, workspace, workspace_bytes, stream);
+}
+
+int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float* rope_cos, const float* rope_sin,
+                           int64_t n_tokens, int64_t attn_chunk_tokens, int64_t mlp_chunk_tokens,
+                           int64_t ffn_chunk_features, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   const int rc = make_plan(h, n_tokens, attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features, &p);
   if (rc != DIT_OK) return rc;
   if (!x || !mod || !workspace) return DIT_EINVAL;
   if (!aligned16(x) || !aligned16(mod) || !aligned16(workspace)) return DIT_EINVAL;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return DIT_EINVAL;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return DIT_EINVAL;
   if (workspace_bytes < p.total) return DIT_ENOSPC;
 
   using namespace dit;
@@ -230,6 +240,9 @@ int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
   const float *sh2 = mod + 3 * d, *sc2 = mod + 4 * d, *g2 = mod + 5 * d;
   const char* wqkv = static_cast<const char*>(h->w.w_qkv);
   const float* s_qkv = w8 ? h->w.s_qkv : nullptr;
+  const int64_t dh = dsc.head_dim, ld_rope = dh / 2;
+  const bool qk_k = h->w.k_norm || rope_cos, qk_q = h->w.q_norm || rope_cos;
+  auto rope_rows = [&](const float* t, int64_t r0) { return t ? t + r0 * ld_rope : nullptr; };
 
   hipError_t err = hipSuccess;
 #define DIT_TRY(kind, call)                                  \
@@ -267,6 +280,10 @@ int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
       g.ldo = p.np;
       DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
     }
+    if (qk_k)
+      DIT_TRY(DIT_K_QK, launch_qk_transform(f32, kbuf + s0 * d * e, d, c, (int)d, (int)dh, h->w.k_norm,
+                                            rope_rows(rope_cos, s0), rope_rows(rope_sin, s0), ld_rope, dsc.eps,
+                                            st));
   }
 
   // ---- pass 2: super-slices of S tokens
@@ -287,6 +304,10 @@ int dit_block_forward(dit_block* h, void* x, const float* mod, int64_t n_tokens,
       g.out = slab_b;
       g.ldo = d;
       DIT_TRY(DIT_K_Q_PROJ, launch_gemm(dt, EPI_STORE, g, st));
+      if (qk_q)
+        DIT_TRY(DIT_K_QK, launch_qk_transform(f32, slab_b, d, c, (int)d, (int)dh, h->w.q_norm,
+                                              rope_rows(rope_cos, s0), rope_rows(rope_sin, s0), ld_rope,
+                                              dsc.eps, st));
       DIT_TRY(DIT_K_ATTENTION, launch_attention(dt, slab_b, d, kbuf, d, vtbuf, p.np, slab_a, d, c, n, (int)dsc.n_heads,
                                (int)dsc.head_dim, st));
       GemmArgs o{};
@@ -398,6 +419,22 @@ int dit_modnorm(int32_t in_dtype, int32_t out_dtype, const void* x, int64_t ldx,
   if (rows == 0) return DIT_OK;
   return hip_status(dit::launch_modnorm(in_dtype == DIT_F32, out_dtype == DIT_F32, x, ldx, shift, scale, out,
                                         ldo, rows, (int)d, eps, static_cast<hipStream_t>(stream)));
+}
+
+int dit_qk_transform(int32_t dtype, void* x, int64_t ldx, int64_t rows, int64_t n_heads, int64_t head_dim,
+                     const float* norm_w, const float* rope_cos, const float* rope_sin, int64_t ld_rope, float eps,
+                     void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EINVAL;
+  if (!x || rows < 0 || n_heads < 1 || (head_dim != 64 && head_dim != 128)) return DIT_EINVAL;
+  const int64_t d = n_heads * head_dim;
+  if (d > 8192 || ldx < d || ldx % 8 || !(eps > 0.f) || !aligned16(x)) return DIT_EINVAL;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return DIT_EINVAL;
+  if (rope_cos && (ld_rope < head_dim / 2 || ld_rope % 4 || !aligned16(rope_cos) || !aligned16(rope_sin)))
+    return DIT_EINVAL;
+  if (norm_w && !aligned16(norm_w)) return DIT_EINVAL;
+  if (rows == 0) return DIT_OK;
+  return hip_status(dit::launch_qk_transform(dtype == DIT_F32, x, ldx, rows, (int)d, (int)head_dim, norm_w,
+                                             rope_cos, rope_sin, ld_rope, eps, static_cast<hipStream_t>(stream)));
 }
 
 int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,

@@ -43,6 +43,11 @@ struct GemmArgs {
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
 hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st);
 
+// Optional QK RMSNorm (w: [head_dim] or null) and RoPE (cs/sn: [rows][ld_rope]
+// or null), in place on `rows` token rows of width d.
+hipError_t launch_qk_transform(int f32, void* x, int64_t ldx, int64_t rows, int d, int head_dim, const float* w,
+                               const float* cs, const float* sn, int64_t ld_rope, float eps, hipStream_t st);
+
 // K3: softmax attention of n_q query rows against n_kv keys for all heads.
 // q [n_q][ldq], k [n_kv][ldk], vt [n_heads*head_dim][ldvt] (V transposed),
 // o [n_q][ldo]; head h owns columns h*head_dim.. of q, k, o and rows of vt.

@@ -155,3 +155,31 @@ def test_planned_chunks_run_within_budget():
         blk.forward(xx, modt, ca, cm, fc, workspace=ws)
         torch.cuda.synchronize()
         check_bf16_bar(to_f64(xx), y_ref)
+
+
+@pytest.mark.parametrize("key", ["bf16", "f32", "w8_bf16", "bf16-dh64"])
+def test_block_with_qk_norm_and_rope(key):
+    shape = SMALL[key]
+    inputs = synth.make_inputs(shape, 0)
+    qk_in = synth.make_qk_inputs(shape, 0)
+    x, mod, w = oracle_inputs(inputs)
+    qk = {k: np.asarray(v, np.float64) for k, v in qk_in.items()}
+    y_ref = O.block_forward(x, mod, w, shape.n_heads, qk=qk)
+    blk, xt, modt = B.block_from_inputs(shape, {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]},
+                                        "cuda")
+    rope = (torch.from_numpy(qk_in["cos"]).cuda(), torch.from_numpy(qk_in["sin"]).cuda())
+    n = shape.n_tokens
+    outs = []
+    for ca, cm in ((256, 256), (0, n), (100, 300)):
+        xx = xt.clone()
+        blk.forward(xx, modt, ca, cm, rope=rope)
+        torch.cuda.synchronize()
+        outs.append(xx.cpu())
+    assert all(bits(o) == bits(outs[0]) for o in outs), "bit-identity with qk-norm and rope"
+    y = to_f64(outs[0])
+    if shape.dtype == "f32":
+        assert max_abs(y, y_ref) <= 1e-4 and rel_l2(y, y_ref) <= 1e-4
+    else:
+        check_bf16_bar(y, y_ref)
+    # the transform matters: without it the output differs from the reference
+    assert max_abs(to_f64(run_block(shape, inputs, 256, 256)), y_ref) > 1e-3

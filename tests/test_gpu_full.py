@@ -106,3 +106,34 @@ def test_full_size_parity_and_bit_identity(name):
     else:
         check_bf16_bar(y, y_ref)
         assert o_rel <= 1e-2
+
+
+def test_full_size_with_qk_norm_and_rope():
+    shape = synth.CONFIGS["large"]
+    n = shape.n_tokens
+    inputs = synth.make_inputs(shape, seed=0)
+    qk_in = synth.make_qk_inputs(shape, 0)
+    blk, x0, mod = B.block_from_inputs(shape, {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]},
+                                       "cuda")
+    rope = (torch.from_numpy(qk_in["cos"]).cuda(), torch.from_numpy(qk_in["sin"]).cuda())
+    digests, y_first = [], None
+    for ca, cm in ((8192, 8192), (5000, 3000)):
+        x = x0.clone()
+        ws = torch.empty(blk.peak_workspace(n, ca, cm, 0), dtype=torch.uint8, device="cuda")
+        blk.forward(x, mod, ca, cm, workspace=ws, rope=rope)
+        torch.cuda.synchronize()
+        digests.append(hashlib.sha256(x.view(torch.uint8).cpu().numpy().tobytes()).hexdigest())
+        if y_first is None:
+            y_first = x.cpu()
+        del x, ws
+    assert digests[0] == digests[1]
+    blk.close()
+    del x0
+    torch.cuda.empty_cache()
+    rows = synth.sample_rows(n, 512)
+    xf, modf, w = oracle_inputs(inputs)
+    qk = {k: np.asarray(v, np.float64) for k, v in qk_in.items()}
+    y_ref = O.block_rows(xf, modf, w, shape.n_heads, rows, eps=shape.eps, qk=qk)
+    y = to_f64(y_first[torch.from_numpy(rows)])
+    print(f"\nlarge+qk: y max_abs={max_abs(y, y_ref):.4g} rel_l2={rel_l2(y, y_ref):.4g}")
+    check_bf16_bar(y, y_ref)

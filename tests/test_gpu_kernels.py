@@ -208,3 +208,29 @@ def test_attention_query_slices_bit_identical():
         B.attention(tq[a:b], tk, tvt, part, 2, n_kv=n_kv)
         torch.cuda.synchronize()
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
+
+
+@pytest.mark.parametrize("dtype,heads,dh,rows", [("bf16", 40, 128, 300), ("bf16", 4, 64, 77), ("f32", 4, 64, 130),
+                                                 ("f32", 2, 128, 33)])
+@pytest.mark.parametrize("mode", ["norm", "rope", "both"])
+def test_qk_transform(dtype, heads, dh, rows, mode):
+    rng = _rng(rows + dh)
+    d = heads * dh
+    t = rng.standard_normal((rows, d)) * 1.5
+    wv = (1.0 + 0.1 * rng.standard_normal(dh)).astype(np.float32)
+    cos, sin = synth.rope_tables(rows, dh, offset=1000)
+    if dtype == "f32":
+        t = t.astype(np.float32).astype(np.float64)
+        x = torch.from_numpy(t.astype(np.float32)).to(DEV)
+    else:
+        t = bf16_round(t)
+        x = _bf16(t)
+    use_norm = mode in ("norm", "both")
+    use_rope = mode in ("rope", "both")
+    B.qk_transform(x, heads, torch.from_numpy(wv).to(DEV) if use_norm else None,
+                   (torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV)) if use_rope else None)
+    ref = O.qk_transform(t, wv.astype(np.float64) if use_norm else None, cos if use_rope else None,
+                         sin if use_rope else None, heads, 1e-6)
+    got = to_f64(x)
+    tol = 1e-5 if dtype == "f32" else 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * tol + tol * 1e-2 * np.abs(ref).max())
