@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
-    "rms_norm_heads", "rope", "qk_transform",
+    "rms_norm_heads", "rope", "qk_transform", "final_layer", "final_layer_chunked",
     "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
 ]
 
@@ -303,3 +303,25 @@ def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.n
         return y
     loc = dict(n1=n1, q=q, k=k[rows], v=v[rows], o=o, x1=x1, n2=n2, h=h)
     return (y,) + tuple(loc[name] for name in want)
+
+
+def final_layer(x: np.ndarray, shift: np.ndarray, scale: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """The output head after the last block: LN(x) * (1 + scale) + shift, then
+    projected by w [out, d]: out[t] = w n[t].
+
+    "LayerStream: H3 Chunking", "How the slicing works": the fp32 output head
+    runs stock and is sliced by tokens only when memory runs out; the streaming
+    proposal's "Summary": final projection/modulation is similarly bounded.
+    """
+    return linear(modulate(layer_norm(x, eps), np.asarray(shift, np.float64), np.asarray(scale, np.float64)), w)
+
+
+def final_layer_chunked(x: np.ndarray, shift: np.ndarray, scale: np.ndarray, w: np.ndarray, chunk: int,
+                        eps: float = 1e-6) -> np.ndarray:
+    """The same head, one slab of ``chunk`` tokens at a time (0 = all tokens)."""
+    n = x.shape[0]
+    c = n if chunk <= 0 else min(chunk, n)
+    out = np.empty((n, w.shape[0]))
+    for s0 in range(0, n, c):
+        out[s0:s0 + c] = final_layer(x[s0:s0 + c], shift, scale, w, eps)
+    return out

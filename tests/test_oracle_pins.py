@@ -293,7 +293,26 @@ def pin_block_qk(M):
         M.matmul = saved
 
 
-PINS = [pin_layer_norm, pin_silu, pin_attention_brute, pin_attention_sdpa, pin_block_torch,
+def pin_final_layer(M):
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((29, 48)) * 2.0
+    sh, sc = rng.standard_normal(48) * 0.3, rng.standard_normal(48) * 0.3
+    wf = rng.standard_normal((16, 48)) / np.sqrt(48)
+    X = torch.from_numpy(x)
+    ref = tF.linear(tF.layer_norm(X, (48,), eps=1e-6) * (1 + torch.from_numpy(sc)) + torch.from_numpy(sh),
+                    torch.from_numpy(wf)).numpy()
+    assert _rel(M.final_layer(x, sh, sc, wf), ref) < 1e-12, "final layer vs torch"
+    saved = M.matmul
+    try:
+        M.matmul = _order_stable
+        full = M.final_layer(x, sh, sc, wf)
+        for c in (1, 5, 28, 0):
+            assert np.array_equal(M.final_layer_chunked(x, sh, sc, wf, c), full), "final layer chunked"
+    finally:
+        M.matmul = saved
+
+
+PINS = [pin_final_layer, pin_layer_norm, pin_silu, pin_attention_brute, pin_attention_sdpa, pin_block_torch,
         pin_chunked_schedule, pin_closed_forms, pin_int8_rows, pin_rows, pin_rms_norm_heads, pin_rope,
         pin_block_qk]
 
@@ -308,7 +327,21 @@ def test_pin_holds(pin):
 
 _orig = {name: getattr(O, name) for name in
          ("layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
-          "block_forward", "block_forward_chunked", "rms_norm_heads", "rope", "qk_transform")}
+          "block_forward", "block_forward_chunked", "rms_norm_heads", "rope", "qk_transform",
+          "final_layer", "final_layer_chunked")}
+
+
+def _final_shift_scale_swapped(x, shift, scale, w, eps=1e-6):
+    return _orig["final_layer"](x, scale, shift, w, eps)
+
+
+def _final_chunk_drops_tail(x, shift, scale, w, chunk, eps=1e-6):
+    n = x.shape[0]
+    c = n if chunk <= 0 else min(chunk, n)
+    out = np.zeros((n, w.shape[0]))
+    for s0 in range(0, n - c + 1, c):  # forgets a ragged last slab
+        out[s0:s0 + c] = _orig["final_layer"](x[s0:s0 + c], shift, scale, w, eps)
+    return out
 
 
 def _rope_sin_flipped(t, cos, sin, n_heads):
@@ -435,6 +468,8 @@ MUTANTS = {
     "rope: halves instead of adjacent pairs": ("rope", _rope_halves),
     "qk-norm: RMS over all of d": ("rms_norm_heads", _rms_over_d),
     "qk: rope before the norm": ("qk_transform", _qk_rope_first),
+    "final layer: shift and scale swapped": ("final_layer", _final_shift_scale_swapped),
+    "final layer: ragged last slab dropped": ("final_layer_chunked", _final_chunk_drops_tail),
 }
 
 
