@@ -1,6 +1,7 @@
 """Benchmark of one token-chunked DiT block forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config large] [--no-cpu-baseline]
+    python bench.py --op final_layer [--steps K] [--warmup W]
 
 A step is one full block forward (pass 1 K/V, pass 2 Q/attention/out-proj,
 SwiGLU MLP) over the whole token sequence, preceded by a device copy that
@@ -85,6 +86,83 @@ def cpu_baseline(shape, inputs, rows: int) -> dict:
             "measured_s": round(t_kv + t_rows, 2), "cpu_count": os.cpu_count()}
 
 
+FINAL_N, FINAL_D, FINAL_OUT = 32768, 5120, 64
+
+
+def bench_final_layer(args) -> int:
+    """The output head after the last block (dit_final_layer): a step is one head
+    call over all tokens: 32768 bf16 token rows of width 5120 (the large block's
+    residual stream) to 64 fp32 outputs each (a 1x2x2 patch of 16 latent channels)."""
+    import numpy as np
+    import torch
+
+    from memory_bounded_chunked_amd import block as B
+    from memory_bounded_chunked_amd import synth
+
+    n, d, od = FINAL_N, FINAL_D, FINAL_OUT
+    dev = "cuda:0"
+    inp = synth.make_final_inputs(n, d, od, "bf16", seed=0)
+    t = {k: B.tensor_from_stored(v, dev) for k, v in inp.items()}
+    out = torch.empty((n, od), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.final_layer(t["x"], t["shift"], t["scale"], t["w_out"], out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    B.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    k_ms, k_n = B.profile_read()["final"]
+    B.profile_enable(False)
+    avg = k_ms / k_n
+    flops = 2.0 * n * d * od
+    achieved = flops / (avg / 1e3) / 1e12
+    hbm_bytes = n * d * 2 + od * d * 4 + 2 * d * 4 + n * od * 4
+    log(f"[bench] final layer: {ms:.4f} ms/step, kernel {avg:.4f} ms, {achieved:.1f} TFLOP/s fp32")
+    result = {
+        "metric": "output-head tokens/s (fp32 modulated LayerNorm + projection) at 32k tokens",
+        "value": round(n / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded PCG64 inputs; see DESIGN.md recipe)",
+        "config": {"workload": f"DiT output head: N={n} bf16 token rows, d={d} -> {od} fp32 outputs, batch 1",
+                   "n_tokens": n, "d": d, "out_dim": od, "workspace_bytes": 0},
+        "roofline": {"kernel": "final_layer", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
+                     "hbm_gbs_algorithmic": round(hbm_bytes / (avg / 1e3) / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        import oracle.dit_block as O
+        rows = min(n, args.cpu_rows * 4)
+        sel = synth.sample_rows(n, rows, seed=1)
+        t0 = time.perf_counter()
+        O.final_layer(synth.to_f64(inp["x"][sel]), inp["shift"].astype(np.float64),
+                      inp["scale"].astype(np.float64), inp["w_out"].astype(np.float64))
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        result["cpu_baseline"] = {"value": round(rows / dt, 1), "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"fp64 oracle head on {rows} sampled token rows ({dt:.2f} s)"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,11 +175,15 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk", action="store_true", help="with QK RMSNorm and RoPE (a widening of the path)")
+    ap.add_argument("--op", choices=("block", "final_layer"), default="block",
+                    help="block forward (default) or the output head after the last block")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the block path is "
               "single-GPU: no collectives)", file=sys.stderr)
         return 2
+    if args.op == "final_layer":
+        return bench_final_layer(args)
 
     import torch
 

@@ -1,7 +1,7 @@
 /*
  * dit_block_profile.h - optional per-kernel timing of dit_block_forward.
  *
- * While enabled, dit_block_forward records a pair of HIP events on its stream
+ * While enabled, dit_block_forward (and dit_final_layer) records a pair of HIP events on its stream
  * around every kernel it enqueues, tagged with the step of the block that the
  * kernel computes. Reading waits for those events and returns the summed
  * elapsed time and the launch count per step. Off by default; when off the
@@ -28,7 +28,8 @@ extern "C" {
 #define DIT_K_GATE_UP 5    /* SwiGLU gate/up projection of an MLP slab */
 #define DIT_K_DOWN 6       /* down projection + gated residual, in place */
 #define DIT_K_QK 7         /* optional QK RMSNorm / RoPE of a Q or K slab */
-#define DIT_K_COUNT 8
+#define DIT_K_FINAL 8      /* dit_final_layer: the output head */
+#define DIT_K_COUNT 9
 
 /* on != 0: clear all records and start recording; on == 0: stop recording
  * (records are kept for dit_profile_read). Returns DIT_OK. */

@@ -1,5 +1,6 @@
-"""Thin ctypes binding over the C ABI in ``include/dit_block.h`` and
-``include/dit_block_steps.h``.
+"""Thin ctypes binding over the C ABI in ``include/dit_block.h``,
+``include/dit_block_steps.h``, ``include/dit_block_profile.h`` and
+``include/dit_final_layer.h``.
 
 Argument marshalling only: every step of the block runs in the HIP library.
 torch supplies device memory and the stream. If the library is not built the
@@ -26,8 +27,8 @@ DEFAULT_MLP_CHUNK = 8192
 
 EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
            "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
-           "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read")
-PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk")
+           "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer")
+PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final")
 
 
 class DitError(RuntimeError):
@@ -81,6 +82,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_attention.restype = ctypes.c_int
     lib.dit_linear.argtypes = [i32, i32, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.dit_linear.restype = ctypes.c_int
+    lib.dit_final_layer.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, i64, vp, i64, ctypes.c_float, vp]
+    lib.dit_final_layer.restype = ctypes.c_int
     lib.dit_profile_enable.argtypes = [ctypes.c_int]
     lib.dit_profile_enable.restype = ctypes.c_int
     lib.dit_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -221,6 +224,22 @@ def linear(dtype: str, epilogue: str, a: torch.Tensor, w: torch.Tensor, out: tor
                           w.stride(0), _ptr(w_scale), up_offset, m, n, k, out.data_ptr(), out.stride(0),
                           _ptr(aux), 0 if aux is None else aux.stride(0), _ptr(gate), _stream(stream)),
            "dit_linear")
+    return out
+
+
+def final_layer(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, w_out: torch.Tensor,
+                out: torch.Tensor | None = None, eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """Output head of the rows of ``x`` [n, d] (fp32 or bf16): modulated LayerNorm, then
+    the fp32 projection by ``w_out`` [out_dim, d] into ``out`` [n, out_dim] fp32 (one kernel)."""
+    lib = load_library()
+    n, d = x.shape
+    out_dim = w_out.shape[0]
+    if out is None:
+        out = torch.empty((n, out_dim), dtype=torch.float32, device=x.device)
+    dt = {torch.float32: 0, torch.bfloat16: 1}[x.dtype]
+    _check(lib.dit_final_layer(dt, x.data_ptr(), x.stride(0), n, d, shift.data_ptr(), scale.data_ptr(),
+                               w_out.data_ptr(), out_dim, out.data_ptr(), out.stride(0), eps, _stream(stream)),
+           "dit_final_layer")
     return out
 
 

@@ -26,6 +26,7 @@
 #include "../../include/dit_block.h"
 #include "../../include/dit_block_profile.h"
 #include "../../include/dit_block_steps.h"
+#include "../../include/dit_final_layer.h"
 #include "kernels.hpp"
 
 struct dit_block {
@@ -486,6 +487,26 @@ int dit_linear(int32_t dtype, int32_t epilogue, const void* a, int64_t lda, cons
   g.gate = gate;
   return hip_status(dit::launch_gemm(dtype, static_cast<dit::Epilogue>(epilogue), g,
                                      static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- output head
+
+int dit_final_layer(int32_t x_dtype, const void* x, int64_t ldx, int64_t n_tokens, int64_t d, const float* shift,
+                    const float* scale, const float* w_out, int64_t out_dim, float* out, int64_t ldo, float eps,
+                    void* stream) {
+  if (x_dtype != DIT_F32 && x_dtype != DIT_BF16) return DIT_EINVAL;
+  if (!shift || !scale || !w_out || n_tokens < 0) return DIT_EINVAL;
+  if (n_tokens > 0 && (!x || !out)) return DIT_EINVAL;  // an empty row range may pass NULL rows
+  if (d < 64 || d > 8192 || d % 64 || out_dim < 1 || out_dim > 128) return DIT_EINVAL;
+  if (ldx < d || ldx % 8 || ldo < out_dim || !(eps > 0.f)) return DIT_EINVAL;
+  if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(w_out)) return DIT_EINVAL;
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return DIT_EINVAL;
+  if (n_tokens == 0) return DIT_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(run_step(DIT_K_FINAL, st, [&] {
+    return dit::launch_final_layer(x_dtype == DIT_F32, x, ldx, n_tokens, (int)d, shift, scale, w_out, (int)out_dim,
+                                   out, ldo, eps, st);
+  }));
 }
 
 }  // extern "C"

@@ -48,6 +48,13 @@ hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t s
 hipError_t launch_qk_transform(int f32, void* x, int64_t ldx, int64_t rows, int d, int head_dim, const float* w,
                                const float* cs, const float* sn, int64_t ld_rope, float eps, hipStream_t st);
 
+// Output head: out[t][j] = sum_c (LN(x[t])[c] * (1 + scale[c]) + shift[c]) * w[j][c],
+// fp32 arithmetic; x [n][ldx] (fp32 or bf16), w [out_dim][d] fp32, out [n][ldo] fp32.
+// d % 64 == 0, 64 <= d <= 8192, 1 <= out_dim <= 128.
+hipError_t launch_final_layer(int x_f32, const void* x, int64_t ldx, int64_t n, int d, const float* shift,
+                              const float* scale, const float* w, int out_dim, float* out, int64_t ldo, float eps,
+                              hipStream_t st);
+
 // K3: softmax attention of n_q query rows against n_kv keys for all heads.
 // q [n_q][ldq], k [n_kv][ldk], vt [n_heads*head_dim][ldvt] (V transposed),
 // o [n_q][ldo]; head h owns columns h*head_dim.. of q, k, o and rows of vt.

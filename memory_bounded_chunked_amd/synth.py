@@ -161,6 +161,25 @@ def make_qk_inputs(shape: BlockShape, seed: int = 0) -> dict:
     return {"q_norm": q_norm, "k_norm": k_norm, "cos": cos, "sin": sin}
 
 
+def make_final_inputs(n_tokens: int, d: int, out_dim: int, act: str = "bf16", seed: int = 0) -> dict:
+    """Inputs of the output head, drawn from PCG64(seed + 2000) in this order:
+    ``x`` [N, d] (bf16 bits or fp32) = N(0, 1) per element plus one N(0, 0.25)
+    offset per row (so row means are far from zero), ``shift`` and ``scale``
+    [d] fp32 ~ N(0, variance 0.1) (like the block's modulation), ``w_out``
+    [out_dim, d] fp32 ~ N(0, variance 1/d)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 2000))
+    step = max(1, _BLOCK_ELEMS // d)
+    x = np.empty((n_tokens, d), dtype=np.uint16 if act == "bf16" else np.float32)
+    for r0 in range(0, n_tokens, step):
+        r1 = min(n_tokens, r0 + step)
+        z = rng.standard_normal((r1 - r0, d)) + 0.5 * rng.standard_normal((r1 - r0, 1))
+        x[r0:r1] = f64_to_bf16_bits(z) if act == "bf16" else z.astype(np.float32)
+    shift = (rng.standard_normal(d) * np.sqrt(0.1)).astype(np.float32)
+    scale = (rng.standard_normal(d) * np.sqrt(0.1)).astype(np.float32)
+    w_out = (rng.standard_normal((out_dim, d)) / np.sqrt(d)).astype(np.float32)
+    return {"x": x, "shift": shift, "scale": scale, "w_out": w_out}
+
+
 def to_f64(arr: np.ndarray) -> np.ndarray:
     """Decode a stored array (bf16 bits, fp32 or int8) exactly to fp64."""
     if arr.dtype == np.uint16:

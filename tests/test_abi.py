@@ -9,7 +9,7 @@ import pytest
 from memory_bounded_chunked_amd import block as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = ["dit_block.h", "dit_block_steps.h", "dit_block_profile.h"]
+HEADERS = sorted(os.listdir(os.path.join(ROOT, "include")))
 
 
 def _declared():
@@ -136,6 +136,33 @@ def test_step_entry_points_reject_before_launch(lib):
     assert lib.dit_linear(1, 2, p, 256, p, 256, None, 0, 10, 256, 256, p, 256, p, 256, None, None) == B.DIT_EINVAL
     assert lib.dit_linear(1, 3, p, 256, p, 256, None, 100, 10, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
     assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+
+
+def test_final_layer_rejects_before_launch(lib):
+    p = 0x10000
+    fl = lib.dit_final_layer
+    # (dtype, x, ldx, n, d, shift, scale, w, out_dim, out, ldo, eps)
+    ok = (1, p, 256, 10, 256, p, p, p, 64, p, 64, 1e-6)
+    assert fl(*ok[:3], 0, *ok[4:], None) == B.DIT_OK  # no rows: nothing enqueued
+    assert fl(1, None, 256, 0, 256, p, p, p, 64, None, 64, 1e-6, None) == B.DIT_OK  # empty range, NULL rows
+    bad = [
+        (2,) + ok[1:],                       # int8 activations are not an input type of the head
+        ok[:1] + (None,) + ok[2:],           # null x
+        ok[:9] + (None,) + ok[10:],          # null out
+        ok[:5] + (None,) + ok[6:],           # null shift
+        ok[:2] + (200,) + ok[3:],            # ldx < d
+        ok[:3] + (-1,) + ok[4:],             # negative n
+        ok[:4] + (96,) + ok[5:],             # d not a multiple of 64
+        ok[:4] + (8256,) + ok[5:],           # d above 8192
+        ok[:8] + (0,) + ok[9:],              # out_dim 0
+        ok[:8] + (129,) + ok[9:],            # out_dim above 128
+        ok[:10] + (63,) + ok[11:],           # ldo < out_dim
+        ok[:11] + (0.0,),                    # eps
+        ok[:7] + (p + 4,) + ok[8:],          # w_out not 16-byte aligned
+        ok[:9] + (p + 2,) + ok[10:],         # out not 4-byte aligned
+    ]
+    for args in bad:
+        assert fl(*args, None) == B.DIT_EINVAL, args
 
 
 def test_profile_read_without_records(lib):

@@ -146,8 +146,10 @@ def test_planned_chunks_run_within_budget():
     n = shape.n_tokens
     floor = blk.peak_workspace(n, 256, 256, 64) - 256 * shape.d * 4 - max(2 * 256 * shape.d * 2,
                                                                           256 * shape.d * 2 + 256 * 64 * 2)
-    for extra in (200_000, 700_000, 10 ** 9):
+    # floor = global K/V; the smallest 256-token plan needs 512 KiB above it at d=256.
+    for extra, expect in ((600_000, (256, 256, 256)), (1_000_000, (256, 256, 0)), (10 ** 9, (0, n, 0))):
         ca, cm, fc = blk.plan_chunks(n, floor + extra)
+        assert (ca, cm, fc) == expect
         need = blk.peak_workspace(n, ca, cm, fc)
         assert need <= floor + extra
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
