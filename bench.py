@@ -26,20 +26,119 @@ METRIC = "DiT-block tokens/s & % bf16 MFMA peak at 32k tokens; peak workspace by
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+FINAL_N, FINAL_D, FINAL_OUT = 32768, 5120, 64
 
 
-def measured_traffic() -> float | None:
-    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE measurement, if the kernel sources are still the measured ones."""
+# HBM traffic records: FETCH_SIZE and WRITE_SIZE of one launch at the bench
+# shape, each scaled by what the same counter reads for a plain copy kernel of
+# known size (``--probe`` runs both; ``--record-traffic`` writes the record).
+COPY_BYTES = 1 << 30  # the calibration kernel reads and writes 1 GiB
+TRAFFIC = {
+    "attention": {
+        "record": "attention_large_32k_traffic.json",
+        "kernel": "dit::attention_bf16_kernel",
+        "sources": ["memory_bounded_chunked_amd/csrc/attention.hip", "memory_bounded_chunked_amd/csrc/common.hpp"],
+        "workload": "8192 query rows x 32768 keys, 40 heads x 128, bf16 (one launch of the 32k-token block)",
+        # Q slab + K + V^T + O, each bf16 [rows][5120]
+        "algorithmic_bytes": (8192 + 32768 + 32768 + 8192) * 5120 * 2,
+    },
+    "final_layer": {
+        "record": "final_layer_32k_traffic.json",
+        "kernel": "dit::final_layer_kernel",
+        "sources": ["memory_bounded_chunked_amd/csrc/final_layer.hip", "memory_bounded_chunked_amd/csrc/common.hpp"],
+        "workload": "output head: 32768 bf16 rows x 5120 -> 64 fp32 outputs",
+        # x bf16 + w_out fp32 + shift/scale fp32 + out fp32
+        "algorithmic_bytes": 32768 * 5120 * 2 + 64 * 5120 * 4 + 2 * 5120 * 4 + 32768 * 64 * 4,
+    },
+}
+
+
+def _sources_sha(files) -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attention_large_32k_traffic.json")
+    return hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in files)).hexdigest()
+
+
+def measured_traffic(kind: str) -> float | None:
+    """HBM bytes per launch of ``kind`` from its committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, if the kernel sources are still the measured ones."""
+    spec = TRAFFIC[kind]
+    path = os.path.join(ROOT, "profiles", spec["record"])
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if _sources_sha(rec["source_files"]) != rec["source_sha256"]:
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+def traffic_probe(kind: str) -> int:
+    """One launch of ``kind`` at the bench shape on random inputs, then the copy
+    kernel used to calibrate the counters (run under rocprofv3 --pmc)."""
+    import torch
+
+    from memory_bounded_chunked_amd import block as B
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    if kind == "attention":
+        d, h, n, ca = 5120, 40, 32768, 8192
+        q = torch.randn(ca, d, device=dev, generator=g).bfloat16()
+        k = torch.randn(n, d, device=dev, generator=g).bfloat16()
+        vt = torch.randn(d, n, device=dev, generator=g).bfloat16()
+        o = torch.empty(ca, d, device=dev, dtype=torch.bfloat16)
+        run = lambda: B.attention(q, k, vt, o, h)  # noqa: E731
+    else:
+        n, d, od = FINAL_N, FINAL_D, FINAL_OUT
+        x = torch.randn(n, d, device=dev, generator=g).bfloat16()
+        sh, sc = torch.randn(d, device=dev, generator=g) * 0.3, torch.randn(d, device=dev, generator=g) * 0.3
+        w = torch.randn(od, d, device=dev, generator=g) / d ** 0.5
+        out = torch.empty(n, od, device=dev)
+        run = lambda: B.final_layer(x, sh, sc, w, out=out)  # noqa: E731
+    a = torch.randn(COPY_BYTES // 4, device=dev, generator=g)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    run()
+    torch.mul(a, 1.0, out=b)  # the copy kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    log(f"[probe] {kind}: one launch + copy kernel done")
+    return 0
+
+
+def record_traffic(kind: str, fetch_csv: str, write_csv: str) -> int:
+    """Write profiles/<record> from the counter_collection.csv of a FETCH_SIZE
+    run and of a WRITE_SIZE run of ``--probe kind`` (host only)."""
+    import csv
+    spec = TRAFFIC[kind]
+
+    def last(path, key):
+        rows = [r for r in csv.DictReader(open(path)) if key in r["Kernel_Name"]]
+        return float(rows[-1]["Counter_Value"])
+
+    fk, wk = last(fetch_csv, spec["kernel"]), last(write_csv, spec["kernel"])
+    cf, cw = last(fetch_csv, "AUnaryFunctor"), last(write_csv, "AUnaryFunctor")
+    fs, ws = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    traffic = fk * 1024 * fs + wk * 1024 * ws
+    rec = {
+        "kernel": spec["kernel"],
+        "workload": spec["workload"],
+        "source_sha256": _sources_sha(spec["sources"]),
+        "source_files": spec["sources"],
+        "fetch_size_kib": fk, "write_size_kib": wk,
+        "copy_kernel": "torch.mul(a, 1.0, out=b) on 1 GiB fp32: reads 1 GiB, writes 1 GiB",
+        "copy_fetch_size_kib": cf, "copy_write_size_kib": cw,
+        "fetch_scale": fs, "write_scale": ws,
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": spec["algorithmic_bytes"],
+        "commands": [f"TMPDIR=/tmp rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic_{kind}_{c} -o t "
+                     f"-- python3 bench.py --probe {kind}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                    + [f"python3 bench.py --record-traffic {kind} <FETCH_SIZE counter_collection.csv> "
+                       f"<WRITE_SIZE counter_collection.csv>"],
+    }
+    path = os.path.join(ROOT, "profiles", spec["record"])
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    log(f"[traffic] {kind}: {traffic / 1e6:.1f} MB per launch (algorithmic {spec['algorithmic_bytes'] / 1e6:.1f} MB)"
+        f" -> {path}")
+    return 0
 
 
 def log(msg: str) -> None:
@@ -84,9 +183,6 @@ def cpu_baseline(shape, inputs, rows: int) -> dict:
                        f"{len(sel)} sampled query rows ({t_rows:.1f} s); full block extrapolated "
                        f"to {t_full:.0f} s"),
             "measured_s": round(t_kv + t_rows, 2), "cpu_count": os.cpu_count()}
-
-
-FINAL_N, FINAL_D, FINAL_OUT = 32768, 5120, 64
 
 
 def bench_final_layer(args) -> int:
@@ -141,7 +237,8 @@ def bench_final_layer(args) -> int:
                    "n_tokens": n, "d": d, "out_dim": od, "workspace_bytes": 0},
         "roofline": {"kernel": "final_layer", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
+                     "traffic": measured_traffic("final_layer"), "avg_launch_ms": round(avg, 4),
+                     "flops_per_launch": flops,
                      "hbm_gbs_algorithmic": round(hbm_bytes / (avg / 1e3) / 1e9, 1)},
         "cpu_baseline": None,
     }
@@ -149,16 +246,19 @@ def bench_final_layer(args) -> int:
         from threadpoolctl import threadpool_info
 
         import oracle.dit_block as O
-        rows = min(n, args.cpu_rows * 4)
-        sel = synth.sample_rows(n, rows, seed=1)
-        t0 = time.perf_counter()
-        O.final_layer(synth.to_f64(inp["x"][sel]), inp["shift"].astype(np.float64),
-                      inp["scale"].astype(np.float64), inp["w_out"].astype(np.float64))
+        # Slabs of 4096 token rows in order, repeated over the sequence until at
+        # least 10 s of oracle work has run.
+        sh, sc, wo = (inp[k].astype(np.float64) for k in ("shift", "scale", "w_out"))
+        rows, r0, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            O.final_layer(synth.to_f64(inp["x"][r0:r0 + 4096]), sh, sc, wo)
+            rows += min(4096, n - r0)
+            r0 = (r0 + 4096) % n
         dt = time.perf_counter() - t0
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         result["cpu_baseline"] = {"value": round(rows / dt, 1), "unit": "tokens/s", "cores": threads,
                                   "kind": "oracle",
-                                  "sample": f"fp64 oracle head on {rows} sampled token rows ({dt:.2f} s)"}
+                                  "sample": f"fp64 oracle head on {rows} token rows in 4096-row slabs ({dt:.1f} s)"}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -177,11 +277,19 @@ def main() -> int:
     ap.add_argument("--qk", action="store_true", help="with QK RMSNorm and RoPE (a widening of the path)")
     ap.add_argument("--op", choices=("block", "final_layer"), default="block",
                     help="block forward (default) or the output head after the last block")
+    ap.add_argument("--probe", choices=tuple(TRAFFIC), default=None,
+                    help="one launch of a kernel plus the calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write the traffic record of KERNEL from two counter_collection.csv files")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the block path is "
               "single-GPU: no collectives)", file=sys.stderr)
         return 2
+    if args.probe:
+        return traffic_probe(args.probe)
     if args.op == "final_layer":
         return bench_final_layer(args)
 
@@ -258,8 +366,7 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(att_tflops / peak, 4) if att_tflops else None,
-        "traffic": (measured_traffic() if args.config == "large" and (ca, cm, fc) == (8192, 8192, 0)
-                    and not args.qk else None),
+        "traffic": (measured_traffic("attention") if args.config == "large" and ca == 8192 else None),
         "avg_launch_ms": round(att_avg_ms, 4) if att_avg_ms else None,
         "flops_per_launch": att_flops_launch,
     }

@@ -14,7 +14,7 @@
  * row t, eps inside the square root. No bias term.
  *
  * Memory: the head is token-wise and this library fuses it into one kernel
- * whose token slab is 32 rows held on chip, so the normalised and modulated
+ * whose token slab is 64 rows per workgroup, so the normalised and modulated
  * rows never exist in device memory: the only device memory touched besides
  * the inputs is `out`. No workspace, no allocation. Since rows are
  * independent, a caller may also call it on any range of rows (x + r0*ldx,
