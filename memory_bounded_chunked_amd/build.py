@@ -56,7 +56,8 @@ def build(verbose: bool = True) -> str:
     if failed:
         raise RuntimeError("HIP compilation failed")
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    # -z defs: a kernel whose host-side stub was not emitted fails here, not at load time
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} in {time.time() - t0:.1f}s")

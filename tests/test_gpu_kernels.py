@@ -210,6 +210,35 @@ def test_attention_query_slices_bit_identical():
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
 
 
+@pytest.mark.parametrize("dh", [64, 128])
+def test_attention_every_tile_count_with_poisoned_padding(dh):
+    # one to six 64-key tiles, full and ragged (every peeled path of the
+    # pipelined kernel); V^T columns past n_kv hold NaN, which must not reach O
+    for n_kv in (1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 383):
+        q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", 70, n_kv, 2, dh, n_kv)
+        tvt[:, n_kv:] = float("nan")
+        out = torch.empty(70, 2 * dh, dtype=tdt, device=DEV)
+        B.attention(tq, tk, tvt, out, 2, n_kv=n_kv)
+        ref = O.attention(q, k, v, 2)
+        got = to_f64(out)
+        assert np.isfinite(got).all(), n_kv
+        assert rel_l2(got, ref) <= 1e-2, n_kv
+
+
+def test_attention_query_slices_bit_identical_sharp_logits():
+    # near one-hot softmax moves the running max many times; each query must
+    # take those decisions from its own scores only, whatever slice holds it
+    n_q, n_kv = 300, 1000
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, 2, 128, 5, scale=3.0)
+    full = torch.empty(n_q, 256, dtype=tdt, device=DEV)
+    B.attention(tq, tk, tvt, full, 2, n_kv=n_kv)
+    for a, b in ((0, 1), (1, 130), (33, 97), (77, 300), (255, 300)):
+        part = torch.empty(b - a, 256, dtype=tdt, device=DEV)
+        B.attention(tq[a:b], tk, tvt, part, 2, n_kv=n_kv)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
+
+
 @pytest.mark.parametrize("dtype,heads,dh,rows", [("bf16", 40, 128, 300), ("bf16", 4, 64, 77), ("f32", 4, 64, 130),
                                                  ("f32", 2, 128, 33)])
 @pytest.mark.parametrize("mode", ["norm", "rope", "both"])
