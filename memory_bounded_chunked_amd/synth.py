@@ -25,8 +25,11 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-__all__ = ["BlockShape", "CONFIGS", "make_inputs", "make_qk_inputs", "rope_tables",
+__all__ = ["BlockShape", "CONFIGS", "make_inputs", "make_qk_inputs", "make_lora", "LORA_TARGETS", "rope_tables",
            "bf16_bits_to_f64", "f64_to_bf16_bits", "sample_rows", "to_f64"]
+
+# Projections an activation-space adapter can attach to, in draw order.
+LORA_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
 
 _BLOCK_ELEMS = 1 << 23  # values per draw call when filling large arrays
 
@@ -178,6 +181,32 @@ def make_final_inputs(n_tokens: int, d: int, out_dim: int, act: str = "bf16", se
     scale = (rng.standard_normal(d) * np.sqrt(0.1)).astype(np.float32)
     w_out = (rng.standard_normal((out_dim, d)) / np.sqrt(d)).astype(np.float32)
     return {"x": x, "shift": shift, "scale": scale, "w_out": w_out}
+
+
+def make_lora(shape: BlockShape, rank, seed: int = 0, targets=LORA_TARGETS, alpha: float = 0.5) -> dict:
+    """Activation-space adapters for ``shape``, drawn from PCG64(seed + 3000).
+
+    For each target in LORA_TARGETS order (targets not asked for are skipped
+    without drawing): ``A`` [rank, in] ~ N(0, variance 1/in), then ``B``
+    [out, rank] ~ N(0, variance 1/rank), stored like the block's activations
+    (fp32 for the "f32" block, bf16 bits otherwise); in/out are d/d for q, k,
+    v, o, d/F for gate and up, F/d for down. ``rank`` is an int or a
+    {target: rank} dict. Returns {target: (A, B, alpha)}.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 3000))
+    act = "f32" if shape.dtype == "f32" else "bf16"
+    d, f = shape.d, shape.ffn
+    dims = {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d), "gate": (d, f), "up": (d, f), "down": (f, d)}
+    out = {}
+    for name in LORA_TARGETS:
+        if name not in targets:
+            continue
+        r = rank[name] if isinstance(rank, dict) else rank
+        n_in, n_out = dims[name]
+        a = _normal(rng, (r, n_in), 1.0 / np.sqrt(n_in), act)
+        b = _normal(rng, (n_out, r), 1.0 / np.sqrt(r), act)
+        out[name] = (a, b, float(np.float32(alpha)))
+    return out
 
 
 def to_f64(arr: np.ndarray) -> np.ndarray:

@@ -22,6 +22,11 @@ branch before its residual add; no biases, no QK-norm, no positional transform,
 no mask; head h owns columns [h*dh, (h+1)*dh) of Q, K and V; scale 1/sqrt(dh);
 SwiGLU = silu(gate) * up with gate rows [0, F) and up rows [F, 2F) of ``w_gu``.
 
+Optional activation-space adapters ("ComfyUI-StaticPipeline", section
+"Activation-space LoRA (bypass mode)"): a projection y = W a becomes
+y = W a + alpha * B (A a) on any of q, k, v, o, gate, up and down, without
+touching W. Pinned against the same block with merged weights W + alpha B A.
+
 Everything is fp64. A library matmul (numpy/OpenBLAS) serves as the matrix
 product step. Parity of every function here is pinned by the CPU tests
 (brute force, torch fp64 library routines, closed forms and invariants).
@@ -33,8 +38,11 @@ import numpy as np
 __all__ = [
     "layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
     "rms_norm_heads", "rope", "qk_transform", "final_layer", "final_layer_chunked",
-    "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
+    "lora_delta", "lora_f64", "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
 ]
+
+# Projections an adapter can attach to, in the block's own names.
+LORA_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
 
 # The matrix-product step. Every product in this module goes through this one
 # name, so a test can substitute an order-stable product.
@@ -154,6 +162,37 @@ def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return np.asarray(s, np.float64)[:, None] * np.asarray(q, np.float64)
 
 
+def lora_delta(a: np.ndarray, ad) -> np.ndarray:
+    """The activation-space adapter term alpha * B (A a) of one projection.
+
+    "ComfyUI-StaticPipeline", section "Activation-space LoRA (bypass mode)":
+    the adapter is applied to activations, y = W x + alpha * B (A x), so the
+    packed (for example int8) weight W is never rewritten. ``ad`` is
+    (A [rank, in], B [out, rank], alpha); None means no adapter (term 0).
+    """
+    if ad is None:
+        return 0.0
+    a_mat, b_mat, alpha = ad
+    return alpha * linear(linear(a, a_mat), b_mat)
+
+
+def lora_f64(lora: dict | None) -> dict:
+    """fp64 copies of the adapters: {target: (A, B, alpha)} for the targets present."""
+    out = {}
+    for name, ad in (lora or {}).items():
+        if name not in LORA_TARGETS:
+            raise ValueError(f"unknown adapter target {name!r}")
+        if ad is not None:
+            a_mat, b_mat, alpha = ad
+            out[name] = (np.asarray(a_mat, np.float64), np.asarray(b_mat, np.float64), float(alpha))
+    return out
+
+
+def _adapter_rows(ad, r0: int, r1: int):
+    """The adapter restricted to output rows [r0, r1) (B rows; A unchanged)."""
+    return None if ad is None else (ad[0], ad[1][r0:r1], ad[2])
+
+
 def block_weights_f64(w: dict) -> dict:
     """fp64 weight matrices from already-decoded arrays (dequantising int8 ones)."""
     out = {}
@@ -171,16 +210,27 @@ def _split(w: dict, d: int):
     return wqkv[:d], wqkv[d:2 * d], wqkv[2 * d:3 * d]
 
 
-def _mlp_delta(n2: np.ndarray, w: dict, ffn: int, f0: int = 0, f1: int | None = None) -> np.ndarray:
-    """W_down[:, f0:f1] (silu(W_gate[f0:f1] n2) * (W_up[f0:f1] n2)) for FFN features [f0, f1)."""
+def _mlp_hidden(n2: np.ndarray, w: dict, ffn: int, f0: int, f1: int, lora: dict) -> np.ndarray:
+    """silu(gate) * up for FFN features [f0, f1), each projection with its adapter."""
+    g = linear(n2, w["gu"][f0:f1]) + lora_delta(n2, _adapter_rows(lora.get("gate"), f0, f1))
+    u = linear(n2, w["gu"][ffn + f0:ffn + f1]) + lora_delta(n2, _adapter_rows(lora.get("up"), f0, f1))
+    return silu(g) * u
+
+
+def _mlp_delta(n2: np.ndarray, w: dict, ffn: int, f0: int = 0, f1: int | None = None,
+               lora: dict | None = None) -> np.ndarray:
+    """W_down[:, f0:f1] h[f0:f1] for FFN features [f0, f1), h = silu(gate) * up.
+
+    The down projection's adapter is not included: its A acts on all of h, so
+    a feature-sliced schedule accumulates A h over the slices (see
+    block_forward_chunked)."""
     f1 = ffn if f1 is None else f1
-    g = linear(n2, w["gu"][f0:f1])
-    u = linear(n2, w["gu"][ffn + f0:ffn + f1])
-    return linear(silu(g) * u, w["down"][:, f0:f1])
+    return linear(_mlp_hidden(n2, w, ffn, f0, f1, lora or {}), w["down"][:, f0:f1])
 
 
 def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
-                  eps: float = 1e-6, want: tuple = (), qk: dict | None = None) -> np.ndarray | tuple:
+                  eps: float = 1e-6, want: tuple = (), qk: dict | None = None,
+                  lora: dict | None = None) -> np.ndarray | tuple:
     """Unchunked block forward; returns y [N, d] (and the named intermediates).
 
     n1 = modulate(LN(x); shift1, scale1);  q, k, v = n1 W_{q,k,v}^T
@@ -189,24 +239,27 @@ def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
     y  = x1 + gate2 * (h W_down^T)
     ``want`` may name any of n1, q, k, v, o, x1, n2, h. ``qk`` optionally holds
     ``q_norm`` / ``k_norm`` ([dh] RMSNorm weights) and ``cos`` / ``sin``
-    ([N, dh/2] RoPE tables), applied to q and k before attention.
+    ([N, dh/2] RoPE tables), applied to q and k before attention. ``lora``
+    optionally maps targets q, k, v, o, gate, up, down to adapters (A, B,
+    alpha), each adding alpha * B (A a) to its projection of a.
     """
     d = x.shape[1]
     ffn = w["down"].shape[1]
     sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
     wq, wk, wv = _split(w, d)
+    lo = lora or {}
     n1 = modulate(layer_norm(x, eps), sh1, sc1)
-    q, k, v = linear(n1, wq), linear(n1, wk), linear(n1, wv)
+    q = linear(n1, wq) + lora_delta(n1, lo.get("q"))
+    k = linear(n1, wk) + lora_delta(n1, lo.get("k"))
+    v = linear(n1, wv) + lora_delta(n1, lo.get("v"))
     if qk:
         q = qk_transform(q, qk.get("q_norm"), qk.get("cos"), qk.get("sin"), n_heads, eps)
         k = qk_transform(k, qk.get("k_norm"), qk.get("cos"), qk.get("sin"), n_heads, eps)
     o = attention(q, k, v, n_heads)
-    x1 = x + g1 * linear(o, w["o"])
+    x1 = x + g1 * (linear(o, w["o"]) + lora_delta(o, lo.get("o")))
     n2 = modulate(layer_norm(x1, eps), sh2, sc2)
-    g = linear(n2, w["gu"][:ffn])
-    u = linear(n2, w["gu"][ffn:])
-    h = silu(g) * u
-    y = x1 + g2 * linear(h, w["down"])
+    h = _mlp_hidden(n2, w, ffn, 0, ffn, lo)
+    y = x1 + g2 * (linear(h, w["down"]) + lora_delta(h, lo.get("down")))
     if not want:
         return y
     loc = dict(n1=n1, q=q, k=k, v=v, o=o, x1=x1, n2=n2, h=h)
@@ -215,7 +268,7 @@ def block_forward(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
 
 def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
                           attn_chunk: int, mlp_chunk: int, ffn_chunk: int = 0,
-                          eps: float = 1e-6, qk: dict | None = None) -> np.ndarray:
+                          eps: float = 1e-6, qk: dict | None = None, lora: dict | None = None) -> np.ndarray:
     """The pages' two-pass, token-chunked schedule of the same block, in place.
 
     Follows "How the slicing works" (LayerStream: H3 Chunking) and "Attention
@@ -228,7 +281,8 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
       MLP:    for each slab of ``mlp_chunk`` tokens, norm2, SwiGLU and add the
               gated result in place; with ``ffn_chunk`` > 0 the FFN features
               are taken a slice at a time and the down-projected partials
-              accumulated ("MLP planning").
+              accumulated ("MLP planning"). An adapter on the down projection
+              then accumulates its A h over the slices too and applies B once.
     ``attn_chunk`` = 0 means one slice of all N tokens. The input is not
     modified; the returned array is the residual stream after the block.
     """
@@ -239,6 +293,7 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
     fc = ffn if ffn_chunk <= 0 else min(ffn_chunk, ffn)
     sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
     wq, wk, wv = _split(w, d)
+    lo = lora or {}
     res = np.array(x, dtype=np.float64, copy=True)
 
     k = np.empty((n, d))
@@ -252,27 +307,37 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
     for s0 in range(0, n, ca):                      # pass 1: K and V only
         s1 = min(n, s0 + ca)
         n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
-        k[s0:s1] = qk_transform(linear(n1, wk), qk.get("k_norm"), rows(cos, s0, s1), rows(sin, s0, s1),
-                                n_heads, eps)
-        v[s0:s1] = linear(n1, wv)
+        k[s0:s1] = qk_transform(linear(n1, wk) + lora_delta(n1, lo.get("k")), qk.get("k_norm"),
+                                rows(cos, s0, s1), rows(sin, s0, s1), n_heads, eps)
+        v[s0:s1] = linear(n1, wv) + lora_delta(n1, lo.get("v"))
     for s0 in range(0, n, ca):                      # pass 2: Q slice vs global K/V
         s1 = min(n, s0 + ca)
         n1 = modulate(layer_norm(res[s0:s1], eps), sh1, sc1)
-        q = qk_transform(linear(n1, wq), qk.get("q_norm"), rows(cos, s0, s1), rows(sin, s0, s1), n_heads, eps)
+        q = qk_transform(linear(n1, wq) + lora_delta(n1, lo.get("q")), qk.get("q_norm"), rows(cos, s0, s1),
+                         rows(sin, s0, s1), n_heads, eps)
         o = attention(q, k, v, n_heads)
-        res[s0:s1] += g1 * linear(o, w["o"])
+        res[s0:s1] += g1 * (linear(o, w["o"]) + lora_delta(o, lo.get("o")))
     for m0 in range(0, n, cm):                      # MLP, token slabs
         m1 = min(n, m0 + cm)
         n2 = modulate(layer_norm(res[m0:m1], eps), sh2, sc2)
         acc = np.zeros((m1 - m0, d))
+        ad = lo.get("down")
+        t = 0.0 if ad is None else np.zeros((m1 - m0, ad[0].shape[0]))
         for f0 in range(0, ffn, fc):                # optional FFN feature slices
-            acc += _mlp_delta(n2, w, ffn, f0, min(ffn, f0 + fc))
+            f1 = min(ffn, f0 + fc)
+            h = _mlp_hidden(n2, w, ffn, f0, f1, lo)
+            acc += linear(h, w["down"][:, f0:f1])
+            if ad is not None:
+                t = t + linear(h, ad[0][:, f0:f1])  # A h, accumulated over the slices
+        if ad is not None:
+            acc += ad[2] * linear(t, ad[1])
         res[m0:m1] += g2 * acc
     return res
 
 
 def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.ndarray,
-               eps: float = 1e-6, want: tuple = (), qk: dict | None = None) -> np.ndarray | tuple:
+               eps: float = 1e-6, want: tuple = (), qk: dict | None = None,
+               lora: dict | None = None) -> np.ndarray | tuple:
     """The block output for the query rows ``rows`` only (exact for those rows).
 
     norm1 and K/V are computed for all N tokens, because every query attends
@@ -283,22 +348,22 @@ def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.n
     sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
     wq, wk, wv = _split(w, d)
     qk = qk or {}
+    lo = lora or {}
     cos, sin = qk.get("cos"), qk.get("sin")
     n1_all = modulate(layer_norm(x, eps), sh1, sc1)
-    k, v = linear(n1_all, wk), linear(n1_all, wv)
+    k = linear(n1_all, wk) + lora_delta(n1_all, lo.get("k"))
+    v = linear(n1_all, wv) + lora_delta(n1_all, lo.get("v"))
     del n1_all
     k = qk_transform(k, qk.get("k_norm"), cos, sin, n_heads, eps)
     xr = x[rows]
     n1 = modulate(layer_norm(xr, eps), sh1, sc1)
-    q = qk_transform(linear(n1, wq), qk.get("q_norm"), None if cos is None else cos[rows],
-                     None if sin is None else sin[rows], n_heads, eps)
+    q = qk_transform(linear(n1, wq) + lora_delta(n1, lo.get("q")), qk.get("q_norm"),
+                     None if cos is None else cos[rows], None if sin is None else sin[rows], n_heads, eps)
     o = attention(q, k, v, n_heads)
-    x1 = xr + g1 * linear(o, w["o"])
+    x1 = xr + g1 * (linear(o, w["o"]) + lora_delta(o, lo.get("o")))
     n2 = modulate(layer_norm(x1, eps), sh2, sc2)
-    g = linear(n2, w["gu"][:ffn])
-    u = linear(n2, w["gu"][ffn:])
-    h = silu(g) * u
-    y = x1 + g2 * linear(h, w["down"])
+    h = _mlp_hidden(n2, w, ffn, 0, ffn, lo)
+    y = x1 + g2 * (linear(h, w["down"]) + lora_delta(h, lo.get("down")))
     if not want:
         return y
     loc = dict(n1=n1, q=q, k=k[rows], v=v[rows], o=o, x1=x1, n2=n2, h=h)

@@ -312,7 +312,64 @@ def pin_final_layer(M):
         M.matmul = saved
 
 
-PINS = [pin_final_layer, pin_layer_norm, pin_silu, pin_attention_brute, pin_attention_sdpa, pin_block_torch,
+def _lora_case(dtype="bf16", d=32, heads=2, ffn=96, n=19, rank=16):
+    x, mod, w, heads = _case(d=d, heads=heads, ffn=ffn, n=n, dtype=dtype)
+    sh = synth.BlockShape("t", d, heads, d // heads, ffn, n, dtype)
+    lora = {k: (synth.to_f64(a), synth.to_f64(b), al) for k, (a, b, al) in synth.make_lora(sh, rank).items()}
+    return x, mod, w, heads, lora
+
+
+def _merged(w, lora, d, ffn):
+    """The same block with each adapter folded into its weight: W + alpha B A."""
+    m = {k: np.array(v, copy=True) for k, v in w.items()}
+    rows = {"q": ("qkv", 0), "k": ("qkv", d), "v": ("qkv", 2 * d), "o": ("o", 0),
+            "gate": ("gu", 0), "up": ("gu", ffn), "down": ("down", 0)}
+    for name, (a, b, alpha) in lora.items():
+        key, r0 = rows[name]
+        delta = alpha * (b @ a)
+        m[key][r0:r0 + delta.shape[0]] += delta
+    return m
+
+
+def pin_lora(M):
+    # the adapter term against torch: alpha * linear(linear(a, A), B)
+    rng = np.random.default_rng(17)
+    a_in = rng.standard_normal((9, 40))
+    A, B = rng.standard_normal((16, 40)) / 6.0, rng.standard_normal((24, 16)) / 4.0
+    ref = (0.75 * tF.linear(tF.linear(torch.from_numpy(a_in), torch.from_numpy(A)), torch.from_numpy(B))).numpy()
+    assert _rel(M.lora_delta(a_in, (A, B, 0.75)), ref) < 1e-12, "lora delta vs torch"
+    # activation-space adapters equal the same block with merged weights
+    # W + alpha B A, on every projection at once and in every schedule
+    for dtype in ("bf16", "w8_bf16"):
+        x, mod, w, heads, lora = _lora_case(dtype)
+        d, ffn = x.shape[1], w["down"].shape[1]
+        ref = M.block_forward(x, mod, _merged(w, lora, d, ffn), heads)
+        assert _rel(M.block_forward(x, mod, w, heads, lora=lora), ref) < 1e-12, f"lora vs merged ({dtype})"
+        assert _rel(M.block_forward_chunked(x, mod, w, heads, 5, 7, lora=lora), ref) < 1e-12, "chunked lora"
+        assert _rel(M.block_forward_chunked(x, mod, w, heads, 0, 4, 32, lora=lora), ref) < 1e-12, "ffn-sliced lora"
+        rows = np.array([0, 6, x.shape[0] - 1])
+        assert _rel(M.block_rows(x, mod, w, heads, rows, lora=lora), ref[rows]) < 1e-12, "rows lora"
+        # each adapter alone, on its own projection
+        for name in lora:
+            one = {name: lora[name]}
+            assert _rel(M.block_forward(x, mod, w, heads, lora=one),
+                        M.block_forward(x, mod, _merged(w, one, d, ffn), heads)) < 1e-12, f"lora {name} alone"
+    # zero B: exactly the block without adapters
+    x, mod, w, heads, lora = _lora_case("bf16")
+    zero = {k: (a, np.zeros_like(b), al) for k, (a, b, al) in lora.items()}
+    assert np.array_equal(M.block_forward(x, mod, w, heads, lora=zero), M.block_forward(x, mod, w, heads)), "zero B"
+    # the chunked schedule is bitwise when the matrix product is order-stable
+    saved = M.matmul
+    try:
+        M.matmul = _order_stable
+        y = M.block_forward(x, mod, w, heads, lora=lora)
+        for ca, cm in ((5, 7), (0, 19), (3, 2)):
+            assert np.array_equal(M.block_forward_chunked(x, mod, w, heads, ca, cm, lora=lora), y), "chunked lora bits"
+    finally:
+        M.matmul = saved
+
+
+PINS = [pin_final_layer, pin_lora, pin_layer_norm, pin_silu, pin_attention_brute, pin_attention_sdpa, pin_block_torch,
         pin_chunked_schedule, pin_closed_forms, pin_int8_rows, pin_rows, pin_rms_norm_heads, pin_rope,
         pin_block_qk]
 
@@ -328,7 +385,40 @@ def test_pin_holds(pin):
 _orig = {name: getattr(O, name) for name in
          ("layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
           "block_forward", "block_forward_chunked", "rms_norm_heads", "rope", "qk_transform",
-          "final_layer", "final_layer_chunked")}
+          "final_layer", "final_layer_chunked", "lora_delta", "_mlp_hidden")}
+
+
+def _lora_alpha_dropped(a, ad):
+    return 0.0 if ad is None else O.linear(O.linear(a, ad[0]), ad[1])
+
+
+def _lora_alpha_twice(a, ad):
+    return 0.0 if ad is None else ad[2] * _orig["lora_delta"](a, ad)
+
+
+def _lora_factors_swapped(a, ad):
+    # B's transpose as the down factor and A's transpose as the up factor
+    return 0.0 if ad is None else ad[2] * O.linear(O.linear(a, ad[1].T), ad[0].T)
+
+
+def _mlp_hidden_adapters_swapped(n2, w, ffn, f0, f1, lora):
+    sw = dict(lora)
+    sw["gate"], sw["up"] = lora.get("up"), lora.get("gate")
+    return _orig["_mlp_hidden"](n2, w, ffn, f0, f1, {k: v for k, v in sw.items() if v is not None})
+
+
+def _chunked_down_adapter_last_slice(x, mod, w, n_heads, attn_chunk, mlp_chunk, ffn_chunk=0, eps=1e-6, qk=None,
+                                     lora=None):
+    # the down adapter sees only the last FFN feature slice of h
+    if not lora or "down" not in lora or ffn_chunk <= 0:
+        return _orig["block_forward_chunked"](x, mod, w, n_heads, attn_chunk, mlp_chunk, ffn_chunk, eps, qk, lora)
+    a, b, al = lora["down"]
+    ffn = w["down"].shape[1]
+    f0 = (ffn - 1) // ffn_chunk * ffn_chunk
+    cut = dict(lora)
+    cut["down"] = (np.where(np.arange(ffn)[None, :] >= f0, a, 0.0), b, al)
+    return _orig["block_forward_chunked"](x, mod, w, n_heads, attn_chunk, mlp_chunk, ffn_chunk, eps, qk, cut)
+
 
 
 def _final_shift_scale_swapped(x, shift, scale, w, eps=1e-6):
@@ -470,6 +560,11 @@ MUTANTS = {
     "qk: rope before the norm": ("qk_transform", _qk_rope_first),
     "final layer: shift and scale swapped": ("final_layer", _final_shift_scale_swapped),
     "final layer: ragged last slab dropped": ("final_layer_chunked", _final_chunk_drops_tail),
+    "lora: alpha dropped": ("lora_delta", _lora_alpha_dropped),
+    "lora: alpha applied twice": ("lora_delta", _lora_alpha_twice),
+    "lora: factors transposed and swapped": ("lora_delta", _lora_factors_swapped),
+    "lora: gate and up adapters swapped": ("_mlp_hidden", _mlp_hidden_adapters_swapped),
+    "lora: down adapter sees only the last FFN slice": ("block_forward_chunked", _chunked_down_adapter_last_slice),
 }
 
 
