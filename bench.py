@@ -275,6 +275,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk", action="store_true", help="with QK RMSNorm and RoPE (a widening of the path)")
+    ap.add_argument("--lora", type=int, default=0, metavar="RANK",
+                    help="with rank-RANK activation-space adapters on all seven projections (a widening)")
     ap.add_argument("--op", choices=("block", "final_layer"), default="block",
                     help="block forward (default) or the output head after the last block")
     ap.add_argument("--probe", choices=tuple(TRAFFIC), default=None,
@@ -312,6 +314,13 @@ def main() -> int:
         inputs = {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]}
         rope = (torch.from_numpy(qk_in["cos"]).to(dev), torch.from_numpy(qk_in["sin"]).to(dev))
     blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
+    lora_flops = 0.0
+    if args.lora:
+        lora = synth.make_lora(shape, args.lora, seed=0)
+        blk.set_lora({k: (B.tensor_from_stored(a, dev), B.tensor_from_stored(b, dev), al)
+                      for k, (a, b, al) in lora.items()})
+        # A then B of each adapter: 2*N*r*(in + out) over q, k, v, o (d, d), gate, up (d, F), down (F, d)
+        lora_flops = 2.0 * shape.n_tokens * args.lora * (11 * shape.d + 3 * shape.ffn)
     x = x0.clone()
     ws_bytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -386,12 +395,14 @@ def main() -> int:
         "config": {
             "workload": (f"{shape.name} DiT block forward: d={d}, {shape.n_heads}x{shape.head_dim} heads, "
                          f"SwiGLU F={shape.ffn}, N={n} tokens, batch 1"
-                         + (", QK RMSNorm + RoPE" if args.qk else "")),
+                         + (", QK RMSNorm + RoPE" if args.qk else "")
+                         + (f", rank-{args.lora} adapters on q/k/v/o/gate/up/down" if args.lora else "")),
             "n_tokens": n, "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
             "peak_workspace_bytes": ws_bytes,
             "tflops": round(tflops, 1),
             "frac_bf16_peak": round(tflops / peak, 4),
             "flops_per_step": flops,
+            **({"lora_rank": args.lora, "lora_flops_per_step": lora_flops} if args.lora else {}),
         },
         "roofline": roofline,
         "kernels": kernels,
@@ -400,7 +411,7 @@ def main() -> int:
     blk.close()
     del x, x0, ws
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.lora:
         log("[bench] cpu_baseline: fp64 oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_rows)
         log(f"[bench] cpu_baseline done: {result['cpu_baseline']['sample']}")

@@ -168,6 +168,42 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
                            int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* One activation-space adapter ("ComfyUI-StaticPipeline", section
+ * "Activation-space LoRA (bypass mode)"): a projection y = W a of the block
+ * becomes y = W a + alpha * B (A a), applied to activations so that W stays
+ * as stored (int8 weights stay packed int8).
+ *   a      device [rank][in], row-major, activation type (fp32 for DIT_F32,
+ *          bf16 for DIT_BF16 and DIT_W8_BF16), 16-byte aligned
+ *   b      device [out][rank], row-major, same type, 16-byte aligned
+ *   rank   0 = no adapter on this projection; else a multiple of 16, <= 256
+ *   alpha  the adapter's scale (finite)
+ * (in, out) are (d, d) for q, k, v and o, (d, F) for gate and up, (F, d) for
+ * down. On the GPU, t = alpha * (A a) is formed in fp32 by a small GEMM and
+ * rounded to the activation type where it enters the projection's MFMA
+ * contraction, which adds B t to W a in the same fp32 accumulator (int8
+ * weights: after their per-row scale); the projection's output is rounded
+ * once, as without an adapter. */
+typedef struct dit_lora {
+  const void* a;
+  const void* b;
+  int64_t rank;
+  float alpha;
+} dit_lora;
+
+typedef struct dit_block_lora {
+  dit_lora q, k, v, o, gate, up, down;
+} dit_block_lora;
+
+/* Attach adapters to the handle (pointers borrowed like the weights; the
+ * struct itself is copied). NULL, or every rank 0, detaches them. Host
+ * metadata only. With adapters attached, dit_block_peak_workspace grows by
+ *   round_up(4 * max(Ca * max(rk + rv, rq, ro), Cm * (rgate + rup + rdown)), 256)
+ * bytes (fp32 t of the adapters of one launch group), placed after the other
+ * regions. Errors: DIT_EINVAL for a null handle, a rank that is negative, not
+ * a multiple of 16 or above 256, a null or misaligned a/b of a present
+ * adapter, or a non-finite alpha; the attached set is then unchanged. */
+int dit_block_set_lora(dit_block* h, const dit_block_lora* lora);
+
 /* Release the handle (host memory only; the weights stay the caller's). */
 void dit_block_destroy(dit_block* h);
 

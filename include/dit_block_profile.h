@@ -29,7 +29,8 @@ extern "C" {
 #define DIT_K_DOWN 6       /* down projection + gated residual, in place */
 #define DIT_K_QK 7         /* optional QK RMSNorm / RoPE of a Q or K slab */
 #define DIT_K_FINAL 8      /* dit_final_layer: the output head */
-#define DIT_K_COUNT 9
+#define DIT_K_LORA 9       /* adapter inputs t = alpha * (A a) of one launch group */
+#define DIT_K_COUNT 10
 
 /* on != 0: clear all records and start recording; on == 0: stop recording
  * (records are kept for dit_profile_read). Returns DIT_OK. */

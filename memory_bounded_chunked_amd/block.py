@@ -27,8 +27,9 @@ DEFAULT_MLP_CHUNK = 8192
 
 EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
            "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
-           "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer")
-PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final")
+           "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer",
+           "dit_block_set_lora")
+PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final", "lora")
 
 
 class DitError(RuntimeError):
@@ -47,6 +48,17 @@ class _Weights(ctypes.Structure):
                 ("w_down", ctypes.c_void_p), ("s_qkv", ctypes.c_void_p), ("s_o", ctypes.c_void_p),
                 ("s_gu", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("q_norm", ctypes.c_void_p),
                 ("k_norm", ctypes.c_void_p)]
+
+
+class _Lora(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("rank", ctypes.c_int64), ("alpha", ctypes.c_float)]
+
+
+class _BlockLora(ctypes.Structure):
+    _fields_ = [(name, _Lora) for name in ("q", "k", "v", "o", "gate", "up", "down")]
+
+
+LORA_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -72,6 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_block_forward_rope.restype = ctypes.c_int
     lib.dit_qk_transform.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, vp, i64, ctypes.c_float, vp]
     lib.dit_qk_transform.restype = ctypes.c_int
+    lib.dit_block_set_lora.argtypes = [vp, ctypes.POINTER(_BlockLora)]
+    lib.dit_block_set_lora.restype = ctypes.c_int
     lib.dit_block_destroy.argtypes = [vp]
     lib.dit_block_destroy.restype = None
     lib.dit_block_strerror.argtypes = [ctypes.c_int]
@@ -133,6 +147,24 @@ class DitBlock:
         _check(self._lib.dit_block_create(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(h)),
                "dit_block_create")
         self._h = h
+
+    def set_lora(self, adapters: dict | None) -> None:
+        """Attach activation-space adapters: ``{target: (A, B, alpha)}`` for targets
+        among q, k, v, o, gate, up, down, with A [rank, in] and B [out, rank]
+        device tensors in the activation type (see ``dit_block_set_lora``).
+        ``None`` or ``{}`` detaches. The tensors stay referenced by the block."""
+        if not adapters:
+            _check(self._lib.dit_block_set_lora(self._h, None), "dit_block_set_lora")
+            self._lora = {}
+            return
+        unknown = set(adapters) - set(LORA_TARGETS)
+        if unknown:
+            raise ValueError(f"unknown adapter targets {sorted(unknown)}")
+        st = _BlockLora()
+        for name, (a, b, alpha) in adapters.items():
+            setattr(st, name, _Lora(a.data_ptr(), b.data_ptr(), a.shape[0], float(alpha)))
+        _check(self._lib.dit_block_set_lora(self._h, ctypes.byref(st)), "dit_block_set_lora")
+        self._lora = dict(adapters)
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -32,6 +33,7 @@
 struct dit_block {
   dit_block_desc desc;
   dit_block_weights w;
+  dit_block_lora lora;  // rank 0 = no adapter
 };
 
 namespace {
@@ -44,8 +46,20 @@ int64_t act_bytes(int dtype) { return dtype == DIT_F32 ? 4 : 2; }
 
 struct Plan {
   int64_t n, ca, cm, fc, s, np;
-  size_t off_k, off_vt, off_stage, off_slab, slab_b, total;
+  size_t off_k, off_vt, off_stage, off_slab, slab_b, off_lora, total;
 };
+
+// Adapter ranks of one handle (0 = none).
+struct Ranks {
+  int64_t q, k, v, o, gate, up, down;
+  int64_t attn() const { return std::max({k + v, q, o}); }  // widest t of one attention launch group
+  int64_t mlp() const { return gate + up + down; }          // t of gate/up and down, live together
+  bool any() const { return q || k || v || o || gate || up || down; }
+};
+Ranks ranks_of(const dit_block* h) {
+  const dit_block_lora& l = h->lora;
+  return {l.q.rank, l.k.rank, l.v.rank, l.o.rank, l.gate.rank, l.up.rank, l.down.rank};
+}
 
 int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chunk, int64_t ffn_chunk,
               Plan* p) {
@@ -64,12 +78,16 @@ int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chu
   const size_t attn_a = round_up((size_t)p->ca * d * e, kAlign);
   const size_t mlp_a = round_up((size_t)p->cm * d * e, kAlign);
   const size_t mlp_h = round_up((size_t)p->cm * p->fc * e, kAlign);
+  const Ranks r = ranks_of(h);
+  const size_t lora_bytes =
+      r.any() ? round_up((size_t)4 * std::max(p->ca * r.attn(), p->cm * r.mlp()), kAlign) : 0;
   p->off_k = 0;
   p->off_vt = k_bytes;
   p->off_stage = p->off_vt + vt_bytes;
   p->off_slab = p->off_stage + stage_bytes;
   p->slab_b = attn_a;  // offset of the Q slab within the slab region
-  p->total = p->off_slab + std::max(2 * attn_a, mlp_a + mlp_h);
+  p->off_lora = p->off_slab + std::max(2 * attn_a, mlp_a + mlp_h);
+  p->total = p->off_lora + lora_bytes;
   return DIT_OK;
 }
 
@@ -147,7 +165,28 @@ int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit
   if (!h) return DIT_EINVAL;
   h->desc = d;
   h->w = *w;
+  std::memset(&h->lora, 0, sizeof(h->lora));
   *out = h;
+  return DIT_OK;
+}
+
+int dit_block_set_lora(dit_block* h, const dit_block_lora* lora) {
+  if (!h) return DIT_EINVAL;
+  if (!lora) {
+    std::memset(&h->lora, 0, sizeof(h->lora));
+    return DIT_OK;
+  }
+  const dit_lora* all[7] = {&lora->q, &lora->k, &lora->v, &lora->o, &lora->gate, &lora->up, &lora->down};
+  for (const dit_lora* l : all) {
+    if (l->rank < 0 || l->rank % 16 || l->rank > 256) return DIT_EINVAL;
+    if (l->rank == 0) continue;
+    if (!l->a || !l->b || !aligned16(l->a) || !aligned16(l->b)) return DIT_EINVAL;
+    if (!std::isfinite(l->alpha)) return DIT_EINVAL;
+  }
+  h->lora = *lora;
+  dit_lora* mine[7] = {&h->lora.q, &h->lora.k, &h->lora.v, &h->lora.o, &h->lora.gate, &h->lora.up, &h->lora.down};
+  for (dit_lora* l : mine)
+    if (l->rank == 0) *l = dit_lora{nullptr, nullptr, 0, 0.f};
   return DIT_OK;
 }
 
@@ -252,6 +291,47 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
     if (err != hipSuccess) return DIT_EHIP;                  \
   } while (0)
 
+  // Activation-space adapters: t = alpha * (A a) of one launch group, fp32
+  // [rows][ldt] at column offset toff of the adapter region; `accumulate`
+  // adds into t (the down adapter over FFN feature slices). A rank-0 adapter
+  // launches nothing.
+  const dit_block_lora& lo = h->lora;
+  const Ranks rk = ranks_of(h);
+  float* tbuf = reinterpret_cast<float*>(ws + p.off_lora);
+  const int lora_dt = f32 ? DIT_F32 : DIT_BF16;  // adapters are never int8
+  auto lora_in = [&](const dit_lora& ad, const void* a, int64_t lda, int64_t rows, int64_t in, int64_t col0,
+                     int64_t ld_in, int64_t ldt, int64_t toff, int accumulate) -> hipError_t {
+    if (ad.rank == 0) return hipSuccess;
+    GemmArgs g{};
+    g.a = a;
+    g.lda = lda;
+    g.M = rows;
+    g.K = in;
+    g.b = static_cast<const char*>(ad.a) + col0 * e;
+    g.ldb = ld_in;
+    g.N = (ad.rank + 63) / 64 * 64;
+    g.n_valid = ad.rank;
+    g.out = tbuf + toff;
+    g.ldo = ldt;
+    g.alpha = ad.alpha;
+    g.accumulate = accumulate;
+    return launch_gemm(lora_dt, EPI_LORA_T, g, st);
+  };
+  auto with_lora = [&](GemmArgs& g, const dit_lora& a0, int64_t b0_row, const dit_lora* a1, int64_t b1_row,
+                       int64_t ldt, int64_t toff1) {
+    if (a0.rank == 0 && (!a1 || a1->rank == 0)) return;
+    g.lora_t = tbuf;
+    g.lora_ldt = ldt;
+    g.lora_b[0] = a0.rank ? static_cast<const char*>(a0.b) + b0_row * a0.rank * e : nullptr;
+    g.lora_r[0] = a0.rank;
+    g.lora_toff[0] = 0;
+    if (a1) {
+      g.lora_b[1] = a1->rank ? static_cast<const char*>(a1->b) + b1_row * a1->rank * e : nullptr;
+      g.lora_r[1] = a1->rank;
+      g.lora_toff[1] = toff1;
+    }
+  };
+
   // ---- pass 1: K and V for all tokens, in slabs of Ca tokens
   for (int64_t s0 = 0; s0 < n; s0 += p.ca) {
     const int64_t c = std::min(p.ca, n - s0);
@@ -266,19 +346,29 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
     g.bscale = s_qkv ? s_qkv + d : nullptr;
     g.out = kbuf + s0 * d * e;
     g.ldo = d;
+    const int64_t ldt_kv = rk.k + rk.v;
+    if (lo.k.rank || lo.v.rank) {
+      if (lo.k.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.k, slab_a, d, c, d, 0, d, ldt_kv, 0, 0));
+      if (lo.v.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.v, slab_a, d, c, d, 0, d, ldt_kv, rk.k, 0));
+    }
     if (d % 256 == 0) {  // one launch: K row-major, V transposed
       g.N = 2 * d;
       g.out2 = vtbuf + s0 * e;
       g.ldo2 = p.np;
       g.split = d;
+      with_lora(g, lo.k, 0, &lo.v, 0, ldt_kv, rk.k);
       DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_KV, g, st));
     } else {
       g.N = d;
-      DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE, g, st));
+      GemmArgs gk = g;
+      with_lora(gk, lo.k, 0, nullptr, 0, ldt_kv, 0);
+      DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE, gk, st));
       g.b = wqkv + 2 * d * d * wb;
       g.bscale = s_qkv ? s_qkv + 2 * d : nullptr;
       g.out = vtbuf + s0 * e;
       g.ldo = p.np;
+      with_lora(g, lo.v, 0, nullptr, 0, ldt_kv, 0);
+      if (g.lora_t) g.lora_t = tbuf + rk.k;  // V's t columns follow K's
       DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
     }
     if (qk_k)
@@ -304,6 +394,8 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       g.bscale = s_qkv;
       g.out = slab_b;
       g.ldo = d;
+      if (lo.q.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.q, slab_a, d, c, d, 0, d, rk.q, 0, 0));
+      with_lora(g, lo.q, 0, nullptr, 0, rk.q, 0);
       DIT_TRY(DIT_K_Q_PROJ, launch_gemm(dt, EPI_STORE, g, st));
       if (qk_q)
         DIT_TRY(DIT_K_QK, launch_qk_transform(f32, slab_b, d, c, (int)d, (int)dh, h->w.q_norm,
@@ -325,6 +417,8 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       o.aux = xb + s0 * d * e;
       o.ldaux = d;
       o.gate = g1;
+      if (lo.o.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.o, slab_a, d, c, d, 0, d, rk.o, 0, 0));
+      with_lora(o, lo.o, 0, nullptr, 0, rk.o, 0);
       DIT_TRY(DIT_K_OUT_PROJ, launch_gemm(dt, EPI_RESID, o, st));
     }
     for (int64_t m0 = t0; m0 < t0 + tn; m0 += p.cm) {
@@ -333,6 +427,10 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       char* n2 = slab_a;
       char* hbuf = slab_a + round_up((size_t)p.cm * d * e, kAlign);
       DIT_TRY(DIT_K_MODNORM, launch_modnorm(1, f32, srows, d, sh2, sc2, n2, d, c, (int)d, dsc.eps, st));
+      // adapter inputs of this slab: [gate | up | down] columns of one t
+      const int64_t ldt_m = rk.mlp();
+      if (lo.gate.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.gate, n2, d, c, d, 0, d, ldt_m, 0, 0));
+      if (lo.up.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.up, n2, d, c, d, 0, d, ldt_m, rk.gate, 0));
       for (int64_t f0 = 0; f0 < ffn; f0 += p.fc) {
         const int64_t fl = std::min(p.fc, ffn - f0);
         GemmArgs gu{};
@@ -347,8 +445,11 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
         gu.bscale = w8 ? h->w.s_gu + f0 : nullptr;
         gu.out = hbuf;
         gu.ldo = p.fc;
+        with_lora(gu, lo.gate, f0, &lo.up, f0, ldt_m, rk.gate);
         DIT_TRY(DIT_K_GATE_UP, launch_gemm(dt, EPI_GATEUP, gu, st));
         const bool last = f0 + fl >= ffn;
+        // the down adapter's A h, accumulated over the feature slices
+        if (lo.down.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.down, hbuf, p.fc, c, fl, f0, ffn, ldt_m, rk.gate + rk.up, f0 > 0));
         GemmArgs dn{};
         dn.a = hbuf;
         dn.lda = p.fc;
@@ -364,6 +465,8 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
           dn.ldo = d;
           dn.aux = srows;
           dn.ldaux = d;
+          with_lora(dn, lo.down, 0, nullptr, 0, ldt_m, 0);
+          if (dn.lora_t) dn.lora_t = tbuf + rk.gate + rk.up;
           DIT_TRY(DIT_K_DOWN, launch_gemm(dt, EPI_FINAL, dn, st));
         } else {
           dn.out = srows;

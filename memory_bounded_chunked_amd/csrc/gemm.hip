@@ -26,6 +26,8 @@
 // Weight-only int8 (W8_BF16): B is int8 in HBM and is widened exactly to bf16
 // on its way into LDS (|q| <= 127 needs 7 significant bits); the per-row scale
 // multiplies the fp32 accumulator in the epilogue.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -136,10 +138,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     aoff[i] = aval[i] ? (uint32_t)((gr - m0) * g.lda * (int64_t)sizeof(TA) + (c & 7) * 16) : 0u;
   }
   const int64_t b_first = b_row(0);
+  bool bval[B_LD];  // EPI_LORA_T: B rows past n_valid read as zero
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int c = tid + i * NTHR;
-    boff[i] = (uint32_t)((b_row(c / B_GROW) - b_first) * g.ldb * (int64_t)sizeof(TB) + (c % B_GROW) * 16);
+    bval[i] = EPI != EPI_LORA_T || b_row(c / B_GROW) < g.n_valid;
+    boff[i] = bval[i] ? (uint32_t)((b_row(c / B_GROW) - b_first) * g.ldb * (int64_t)sizeof(TB) + (c % B_GROW) * 16)
+                      : 0u;
   }
   const char* a_base = A + m0 * g.lda * (int64_t)sizeof(TA);
   const char* b_base = B + b_first * g.ldb * (int64_t)sizeof(TB);
@@ -154,7 +159,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     for (int i = 0; i < A_LD; ++i)
       ra[i] = aval[i] ? *reinterpret_cast<const u32x4*>(at + aoff[i]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bt + boff[i]);
+    for (int i = 0; i < B_LD; ++i)
+      rb[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bt + boff[i]) : u32x4{0u, 0u, 0u, 0u};
   };
   auto store_tiles = [&](int buf) {
     char* As = smem + buf * STAGE;
@@ -188,6 +194,102 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
   const int half = lane >> 5;
+
+  // ---- activation-space adapter phase (see GemmArgs): the adapter term joins
+  // the same fp32 accumulator as the main contraction, so the output is
+  // rounded once. Except for int8 weights it runs first, into the zeroed
+  // accumulator, while no main-loop state is live. A-operand fragments come from t (fp32, rounded to the activation
+  // type here), B-operand fragments from the adapter's B rows, both straight
+  // from global memory (both are small and stay in L2).
+  auto lora_phase = [&]() {
+    if constexpr (EPI != EPI_LORA_T) {
+      // The lane id passes through an empty asm here, so nothing derived from
+      // it is computed before the main loop and held in registers across it.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int l32 = ln & 31, hf = ln >> 5;
+      int64_t brow[NTL], sidx[NTL];
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        if constexpr (EPI == EPI_GATEUP) {
+          const int64_t f = tn * (BN / 2) + ((wn * NTL + j) >> 1) * 32 + l32;
+          brow[j] = f;
+          sidx[j] = f + ((j & 1) ? g.up_offset : 0);
+        } else {
+          const int64_t col = tn * BN + wn * WTN + j * 32 + l32;
+          brow[j] = (EPI == EPI_KV && col >= g.split) ? col - g.split : col;
+          sidx[j] = col;
+        }
+      }
+      if constexpr (B_I8) {  // the weight's per-row scale belongs to W a only
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+          const float sc = g.bscale[sidx[j]];
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
+        }
+      }
+      // One k loop per segment; a tile's columns belong to segment `SG` when
+      // seg[j] == SG (GATEUP: j parity; KV: the whole tile; else segment 0).
+      auto lora_seg = [&](auto sg_c) {
+        constexpr int SG = decltype(sg_c)::value;
+        constexpr int KS = A_F32 ? 2 : 16;  // k per MFMA
+        const int64_t r = g.lora_r[SG];
+        const TA* bbase = static_cast<const TA*>(g.lora_b[SG]);
+        for (int64_t k0 = 0; k0 < r; k0 += KS) {
+          const int64_t kk = g.lora_toff[SG] + k0 + (A_F32 ? hf : 8 * hf);
+          u32x4 bfr[NTL];
+          float bf32[NTL];
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) {
+            if (EPI == EPI_GATEUP && (j & 1) != SG) continue;
+            const TA* bp = bbase + brow[j] * r + k0;
+            if constexpr (A_F32)
+              bf32[j] = load_act(bp + hf);
+            else
+              bfr[j] = *reinterpret_cast<const u32x4*>(bp + 8 * hf);
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 32 + l32;
+            const float* tp = g.lora_t + (row < g.M ? row : 0) * g.lora_ldt + kk;
+            if constexpr (A_F32) {
+              const float av = row < g.M ? *tp : 0.f;
+#pragma unroll
+              for (int j = 0; j < NTL; ++j)
+                if (EPI != EPI_GATEUP || (j & 1) == SG) acc[i][j] = mfma32_f32(av, bf32[j], acc[i][j]);
+            } else {
+              f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+              if (row < g.M) {
+                lo = *reinterpret_cast<const f32x4*>(tp);
+                hi = *reinterpret_cast<const f32x4*>(tp + 4);
+              }
+              const u32x4 af = u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                     pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+#pragma unroll
+              for (int j = 0; j < NTL; ++j)
+                if (EPI != EPI_GATEUP || (j & 1) == SG)
+                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfr[j]),
+                                          acc[i][j]);
+            }
+          }
+        }
+      };
+      if constexpr (EPI == EPI_GATEUP) {
+        lora_seg(std::integral_constant<int, 0>{});
+        lora_seg(std::integral_constant<int, 1>{});
+      } else if constexpr (EPI == EPI_KV) {
+        if (tn * BN < g.split)  // uniform per workgroup: the split is tile-aligned
+          lora_seg(std::integral_constant<int, 0>{});
+        else
+          lora_seg(std::integral_constant<int, 1>{});
+      } else {
+        lora_seg(std::integral_constant<int, 0>{});
+      }
+    }
+  };
 
   const int a_rd = lds_slot(arow, half), b_rd = lds_slot(brow, half);
   auto compute = [&](int buf) {
@@ -224,6 +326,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // before the last barrier, and the staging registers are refilled with
   // tile kt+2. One barrier per k-tile.
   const int KT = (int)(g.K / BK);
+  if constexpr (!B_I8) {
+    if (g.lora_t != nullptr) lora_phase();
+  }
   load_tiles(0);
   store_tiles(0);
   if (KT > 1) load_tiles(BK);
@@ -243,8 +348,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   }
   compute(kt & 1);
 
-  // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
+  // int8 weights: the adapter term joins after the contraction and the
+  // per-row scale (which belongs to W a only) is applied before it.
   const float* bscale = g.bscale;
+  if constexpr (B_I8) {
+    if (g.lora_t != nullptr) {
+      lora_phase();
+      bscale = nullptr;
+    }
+  }
+
+  // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
   if constexpr (EPI == EPI_GATEUP) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -316,6 +430,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     } else {
       store_t(static_cast<TA*>(g.out), g.ldo, 0);
     }
+  } else if constexpr (EPI == EPI_LORA_T) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
+        if (col >= g.n_valid) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row >= g.M) continue;
+          float* o = static_cast<float*>(g.out) + row * g.ldo + col;
+          *o = (g.accumulate ? *o : 0.f) + g.alpha * acc[i][j][r];
+        }
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -385,6 +514,9 @@ static hipError_t launch_types(Epilogue epi, const GemmArgs& g, hipStream_t st) 
     case EPI_ACCUM: return launch_epi<TA, TB, EPI_ACCUM>(g, st);
     case EPI_FINAL: return launch_epi<TA, TB, EPI_FINAL>(g, st);
     case EPI_KV: return launch_epi<TA, TB, EPI_KV>(g, st);
+    case EPI_LORA_T:
+      if constexpr (sizeof(TB) == 1) return hipErrorInvalidValue;  // adapters are never int8
+      else return launch_epi<TA, TB, EPI_LORA_T>(g, st);
   }
   return hipErrorInvalidValue;
 }

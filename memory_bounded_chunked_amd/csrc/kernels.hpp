@@ -20,6 +20,8 @@ enum Epilogue : int {
   EPI_FINAL = 5,    // out[m][n] = aux[m][n] (fp32) + gate[n] * acc     out: activation type
   EPI_KV = 6,       // columns [0, split): out[m][n] = acc; columns [split, N):
                     // out2[n - split][m] = acc (K row-major and V transposed, one launch)
+  EPI_LORA_T = 7,   // adapter input product: out (fp32) [m][n] = (accumulate ? out[m][n] : 0)
+                    // + alpha * acc for n < n_valid; B rows >= n_valid read as zero
 };
 
 struct GemmArgs {
@@ -38,6 +40,22 @@ struct GemmArgs {
   void* out2;           // KV: transposed destination of the columns from `split` on
   int64_t ldo2;
   int64_t split;        // KV: first column stored transposed (a multiple of the tile width)
+  // EPI_LORA_T
+  float alpha;
+  int accumulate;
+  int64_t n_valid;
+  // Activation-space adapter phase of the main epilogues (lora_t == null: none).
+  // After the contraction, output column n of segment s gains
+  //   sum_j t[m][lora_toff[s] + j] * lora_b[s][row_s(n)][j],  j < lora_r[s],
+  // with t fp32 [M][lora_ldt] (rounded to the activation type on use) and
+  // lora_b[s] [rows][lora_r[s]] in the activation type. Segments: KV: 0 = K
+  // columns, 1 = V columns; GATEUP: 0 = gate, 1 = up (row = feature); else 0.
+  // For int8 weights the per-row scale is applied before this phase.
+  const float* lora_t;
+  int64_t lora_ldt;
+  const void* lora_b[2];
+  int64_t lora_r[2];
+  int64_t lora_toff[2];
 };
 
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).

@@ -169,7 +169,7 @@ def test_profile_read_without_records(lib):
     assert lib.dit_profile_enable(1) == 0
     t, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.dit_profile_read(3, ctypes.byref(t), ctypes.byref(n)) == 0 and n.value == 0
-    assert lib.dit_profile_read(9, ctypes.byref(t), ctypes.byref(n)) == B.DIT_EINVAL
+    assert lib.dit_profile_read(len(B.PROFILE_KINDS), ctypes.byref(t), ctypes.byref(n)) == B.DIT_EINVAL
     assert lib.dit_profile_enable(0) == 0
 
 
@@ -232,3 +232,51 @@ def test_plan_chunks_rejects(lib):
     assert lib.dit_block_plan_chunks(h, 0, 1 << 30, ctypes.byref(a), ctypes.byref(a), ctypes.byref(a)) == B.DIT_EINVAL
     assert lib.dit_block_plan_chunks(None, 10, 1 << 30, ctypes.byref(a), ctypes.byref(a), ctypes.byref(a)) == B.DIT_EINVAL
     lib.dit_block_destroy(h)
+
+
+def _lora_struct(ranks, ptr=0x10000, alpha=0.5):
+    st = B._BlockLora()
+    for name, r in ranks.items():
+        setattr(st, name, B._Lora(ptr if r else 0, ptr if r else 0, r, alpha))
+    return st
+
+
+def test_set_lora_validation(lib):
+    rc, h = _handle(lib)
+    assert rc == 0
+    try:
+        ok = _lora_struct({"q": 16, "k": 32, "gate": 64, "down": 256})
+        assert lib.dit_block_set_lora(h, ctypes.byref(ok)) == B.DIT_OK
+        assert lib.dit_block_set_lora(h, None) == B.DIT_OK
+        for bad in ({"q": 8}, {"v": 272}, {"o": -16}, {"up": 17}):
+            assert lib.dit_block_set_lora(h, ctypes.byref(_lora_struct(bad))) == B.DIT_EINVAL, bad
+        assert lib.dit_block_set_lora(h, ctypes.byref(_lora_struct({"q": 16}, ptr=0x10008))) == B.DIT_EINVAL
+        assert lib.dit_block_set_lora(h, ctypes.byref(_lora_struct({"q": 16}, alpha=float("nan")))) == B.DIT_EINVAL
+        null = B._BlockLora()
+        null.k = B._Lora(0x10000, 0, 16, 1.0)  # B missing
+        assert lib.dit_block_set_lora(h, ctypes.byref(null)) == B.DIT_EINVAL
+        assert lib.dit_block_set_lora(None, ctypes.byref(ok)) == B.DIT_EINVAL
+    finally:
+        lib.dit_block_destroy(h)
+
+
+@pytest.mark.parametrize("n,ca,cm,fc", [(1000, 256, 256, 0), (777, 100, 300, 128), (32768, 8192, 8192, 0)])
+def test_workspace_closed_form_with_adapters(lib, n, ca, cm, fc):
+    ranks = {"q": 16, "k": 32, "v": 48, "o": 64, "gate": 16, "up": 32, "down": 128}
+    d, ffn = (5120, 13824) if n >= 32768 else (256, 1024)
+    rc, h = _handle(lib, d=d, heads=d // 128, ffn=ffn, dtype=1)
+    assert rc == 0
+    try:
+        base = _ws(lib, h, n, ca, cm, fc)[1]
+        assert lib.dit_block_set_lora(h, ctypes.byref(_lora_struct(ranks))) == B.DIT_OK
+        rc, got = _ws(lib, h, n, ca, cm, fc)
+        assert rc == 0
+        a = n if ca == 0 else min(ca, n)
+        m = min(cm, n)
+        t = 4 * max(a * max(ranks["k"] + ranks["v"], ranks["q"], ranks["o"]),
+                    m * (ranks["gate"] + ranks["up"] + ranks["down"]))
+        assert got == base + (t + 255) // 256 * 256
+        assert lib.dit_block_set_lora(h, None) == B.DIT_OK
+        assert _ws(lib, h, n, ca, cm, fc)[1] == base
+    finally:
+        lib.dit_block_destroy(h)
