@@ -4,9 +4,9 @@
 // K-contiguous, which is the operand layout MFMA consumes directly. A
 // 256-row tile of A and a BN-row tile of B are staged through LDS (double
 // buffered: the next k-tile's global loads are in flight while the current
-// one is multiplied); each of the 4 wavefronts computes a 128 x BN/2 block
-// with its accumulators in AGPRs, so every 16-byte fragment read from LDS
-// feeds BN/64 (or 4) MFMAs. LDS rows hold 128 B of k and are padded to 144 B:
+// one is multiplied); WM x WN wavefronts (8 for BN = 256 or 128: two per
+// SIMD) each compute a (256/WM) x (BN/WN) block with accumulators in VGPRs.
+// LDS rows hold 128 B of k and are padded to 144 B:
 // consecutive rows start 4 banks apart, so fragment reads are conflict-free
 // and their addresses are a per-lane base plus compile-time offsets.
 //
@@ -107,9 +107,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
 
   constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
-  const int64_t tiles_n = g.N / OUT_BN;
+  const int64_t tiles_n = (g.N - g.col0) / OUT_BN;
   int64_t tm, tn;
   tile_of(blockIdx.x, ceil_div(g.M, BM), tiles_n, tm, tn);
+  tn += g.col0 / OUT_BN;  // this launch covers output columns [col0, N)
   const int64_t m0 = tm * BM;
 
   const char* A = static_cast<const char*>(g.a);
@@ -479,10 +480,44 @@ template <typename TA, typename TB, int EPI, int BN, int WM, int WN>
 static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 256;
   constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
-  const int64_t tiles = ceil_div(g.M, BM) * (g.N / OUT_BN);
+  const int64_t tiles = ceil_div(g.M, BM) * ((g.N - g.col0) / OUT_BN);
   hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0, st,
                      g);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Outputs narrower than 8192 columns: columns [0, na) go in 256x256 tiles and
+// [na, N) in 256x128 tiles, with na chosen so that the two launches fill whole
+// rounds of the compute units. Cost model: one round of 256x256 tiles = 1, one
+// round of 256x128 tiles = 0.6 (measured: 256x128 tiles run ~15% below the
+// 256x256 rate). At 8192 rows and N = 5120 on 256 CUs: na = 4096, i.e. 512 +
+// 256 tiles = 2 + 1 rounds (2.6), against 5 rounds of 256x128 tiles (3.0).
+static int64_t wide_split(int64_t m, int64_t n, int cus) {
+  const int64_t mt = ceil_div(m, (int64_t)256);
+  double best = 1e300;
+  int64_t na_best = 0;
+  for (int64_t na = 0; na <= n; na += 256) {
+    const double c = (double)ceil_div(mt * (na / 256), (int64_t)cus) +
+                     0.6 * (double)ceil_div(mt * ((n - na) / 128), (int64_t)cus);
+    if (c <= best) {  // ties: more 256-wide columns
+      best = c;
+      na_best = na;
+    }
+  }
+  return na_best;
 }
 
 template <typename TA, typename TB, int EPI>
@@ -495,9 +530,24 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
     if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
   } else {
-    // 256-wide tiles only for wide outputs; d-wide outputs (5120) use 128 so
-    // an 8192-row slab gives 1280 tiles: five full rounds over 256 CUs.
+    // 256-wide tiles for wide outputs; narrower ones are split by columns
+    // between 256- and 128-wide tiles (wide_split). Which tile computes an
+    // element does not change its value: the k sequence is the same.
     if (g.N % 256 == 0 && g.N >= 8192) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
+    if constexpr (EPI != EPI_LORA_T && EPI != EPI_KV) {
+      if (g.N % 256 == 0) {
+        const int64_t na = wide_split(g.M, g.N, cu_count());
+        if (na > 0) {
+          GemmArgs ga = g;
+          ga.N = na;
+          const hipError_t e = launch_tile<TA, TB, EPI, 256, 2, 4>(ga, st);
+          if (e != hipSuccess || na == g.N) return e;
+        }
+        GemmArgs gb = g;
+        gb.col0 = na;
+        return launch_tile<TA, TB, EPI, 128, 4, 2>(gb, st);
+      }
+    }
     if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
     if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 64, 4, 1>(g, st);
   }
@@ -521,7 +571,9 @@ static hipError_t launch_types(Epilogue epi, const GemmArgs& g, hipStream_t st) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g_in, hipStream_t st) {
+  GemmArgs g = g_in;
+  g.col0 = 0;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int bk = dtype == F32 ? 32 : 64;
   if (g.K <= 0 || g.K % bk) return hipErrorInvalidValue;

@@ -56,6 +56,8 @@ struct GemmArgs {
   const void* lora_b[2];
   int64_t lora_r[2];
   int64_t lora_toff[2];
+  // Set by launch_gemm only: a launch covers output columns [col0, N).
+  int64_t col0;
 };
 
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
