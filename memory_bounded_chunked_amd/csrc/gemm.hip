@@ -499,20 +499,23 @@ static int cu_count() {
   return cached[dev];
 }
 
-// Outputs narrower than 8192 columns: columns [0, na) go in 256x256 tiles and
-// [na, N) in 256x128 tiles, with na chosen so that the two launches fill whole
-// rounds of the compute units. Cost model: one round of 256x256 tiles = 1, one
-// round of 256x128 tiles = 0.6 (measured: 256x128 tiles run ~15% below the
-// 256x256 rate). At 8192 rows and N = 5120 on 256 CUs: na = 4096, i.e. 512 +
-// 256 tiles = 2 + 1 rounds (2.6), against 5 rounds of 256x128 tiles (3.0).
-static int64_t wide_split(int64_t m, int64_t n, int cus) {
+// Column split between 256-wide B tiles (wb output columns each: 256, or 128
+// features for GATEUP) and 128-wide B tiles (wb/2 columns): columns [0, na)
+// in the first kind, [na, N) in the second, with na chosen so that the two
+// launches fill whole rounds of the compute units. Cost model: one round of
+// 256-wide tiles = 1, one round of 128-wide tiles = 0.6 (measured: 0.58 on
+// the down projection). At 8192 rows on 256 CUs: N = 5120 gives na = 4096,
+// i.e. 512 + 256 tiles = 2 + 1 rounds (2.6) against 5 rounds of 128-wide
+// tiles (3.0); gate/up with F = 13824 gives 13 + 1 rounds (13.6) against
+// 13.5 rounded up to 14.
+static int64_t wide_split(int64_t m, int64_t n, int cus, int64_t wb) {
   const int64_t mt = ceil_div(m, (int64_t)256);
   double best = 1e300;
   int64_t na_best = 0;
-  for (int64_t na = 0; na <= n; na += 256) {
-    const double c = (double)ceil_div(mt * (na / 256), (int64_t)cus) +
-                     0.6 * (double)ceil_div(mt * ((n - na) / 128), (int64_t)cus);
-    if (c <= best) {  // ties: more 256-wide columns
+  for (int64_t na = 0; na <= n; na += wb) {
+    const double c = (double)ceil_div(mt * (na / wb), (int64_t)cus) +
+                     0.6 * (double)ceil_div(mt * ((n - na) / (wb / 2)), (int64_t)cus);
+    if (c <= best) {  // ties: more 256-wide tiles
       best = c;
       na_best = na;
     }
@@ -522,34 +525,32 @@ static int64_t wide_split(int64_t m, int64_t n, int cus) {
 
 template <typename TA, typename TB, int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  // The tile shape depends only on N and the epilogue (never on M), so every
-  // token row takes the same instruction sequence whatever the slab size.
-  // 8 wavefronts (2 per SIMD) per 256-row tile: while one wave waits on LDS
-  // or a barrier, the other keeps the matrix core busy.
-  if constexpr (EPI == EPI_GATEUP) {
-    if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
-    if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
-  } else {
-    // 256-wide tiles for wide outputs; narrower ones are split by columns
-    // between 256- and 128-wide tiles (wide_split). Which tile computes an
-    // element does not change its value: the k sequence is the same.
+  // The tile shapes depend only on M, N and the epilogue, and which tile
+  // computes an element does not change its value (every tile shape runs the
+  // same k sequence), so every token row gets the same bits whatever the slab
+  // size. 8 wavefronts (2 per SIMD) per 256-row tile: while one wave waits on
+  // LDS or a barrier, the other keeps the matrix core busy.
+  if constexpr (EPI == EPI_KV || EPI == EPI_LORA_T) {
     if (g.N % 256 == 0 && g.N >= 8192) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);
-    if constexpr (EPI != EPI_LORA_T && EPI != EPI_KV) {
-      if (g.N % 256 == 0) {
-        const int64_t na = wide_split(g.M, g.N, cu_count());
-        if (na > 0) {
-          GemmArgs ga = g;
-          ga.N = na;
-          const hipError_t e = launch_tile<TA, TB, EPI, 256, 2, 4>(ga, st);
-          if (e != hipSuccess || na == g.N) return e;
-        }
-        GemmArgs gb = g;
-        gb.col0 = na;
-        return launch_tile<TA, TB, EPI, 128, 4, 2>(gb, st);
-      }
-    }
     if (g.N % 128 == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
     if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 64, 4, 1>(g, st);
+  } else {
+    constexpr int64_t WB = (EPI == EPI_GATEUP) ? 128 : 256;  // output columns of a 256-wide B tile
+    if (g.N % WB == 0) {
+      const int64_t na = wide_split(g.M, g.N, cu_count(), WB);
+      if (na > 0) {
+        GemmArgs ga = g;
+        ga.N = na;
+        const hipError_t e = launch_tile<TA, TB, EPI, 256, 2, 4>(ga, st);
+        if (e != hipSuccess || na == g.N) return e;
+      }
+      GemmArgs gb = g;
+      gb.col0 = na;
+      return launch_tile<TA, TB, EPI, 128, 4, 2>(gb, st);
+    }
+    if (g.N % (WB / 2) == 0) return launch_tile<TA, TB, EPI, 128, 4, 2>(g, st);
+    if constexpr (EPI != EPI_GATEUP)
+      if (g.N % 64 == 0) return launch_tile<TA, TB, EPI, 64, 4, 1>(g, st);
   }
   return hipErrorInvalidValue;
 }
