@@ -178,11 +178,13 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
  *   rank   0 = no adapter on this projection; else a multiple of 16, <= 256
  *   alpha  the adapter's scale (finite)
  * (in, out) are (d, d) for q, k, v and o, (d, F) for gate and up, (F, d) for
- * down. On the GPU, t = alpha * (A a) is formed in fp32 by a small GEMM and
- * rounded to the activation type where it enters the projection's MFMA
- * contraction, which adds B t to W a in the same fp32 accumulator (int8
- * weights: after their per-row scale); the projection's output is rounded
- * once, as without an adapter. */
+ * down. On the GPU, t = alpha * (A a) is formed in fp32 (bf16 blocks: by a
+ * kernel whose workgroups own 32 token rows and split the contraction into a
+ * fixed number of contiguous parts, added in a fixed order). The projection's MFMA contraction adds B t to W a in the
+ * same fp32 accumulator (int8 weights: after their per-row scale); for bf16,
+ * t enters it as its bf16 rounding plus the bf16 rounding of the residual, so
+ * the adapter adds no rounding point of its own, and the projection's output
+ * is rounded once, as without an adapter. */
 typedef struct dit_lora {
   const void* a;
   const void* b;

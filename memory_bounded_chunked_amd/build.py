@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdit_block.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["modnorm.hip", "gemm.hip", "attention.hip", "qk_transform.hip", "final_layer.hip", "dit_block.cpp"]
+SOURCES = ["modnorm.hip", "gemm.hip", "attention.hip", "qk_transform.hip", "final_layer.hip", "lora.hip",
+           "dit_block.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

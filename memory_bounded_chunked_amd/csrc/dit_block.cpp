@@ -302,6 +302,9 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
   auto lora_in = [&](const dit_lora& ad, const void* a, int64_t lda, int64_t rows, int64_t in, int64_t col0,
                      int64_t ld_in, int64_t ldt, int64_t toff, int accumulate) -> hipError_t {
     if (ad.rank == 0) return hipSuccess;
+    if (!f32)
+      return launch_lora_t(a, lda, static_cast<const char*>(ad.a) + col0 * e, ld_in, rows, in, ad.rank, ad.alpha,
+                           accumulate, tbuf + toff, ldt, st);
     GemmArgs g{};
     g.a = a;
     g.lda = lda;

@@ -199,9 +199,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // ---- activation-space adapter phase (see GemmArgs): the adapter term joins
   // the same fp32 accumulator as the main contraction, so the output is
   // rounded once. Except for int8 weights it runs first, into the zeroed
-  // accumulator, while no main-loop state is live. A-operand fragments come from t (fp32, rounded to the activation
-  // type here), B-operand fragments from the adapter's B rows, both straight
-  // from global memory (both are small and stay in L2).
+  // accumulator, while no main-loop state is live. A-operand fragments come from t (fp32; for bf16 as a
+  // rounded value plus its residual), B-operand fragments from the adapter's
+  // B rows, both straight from global memory (both are small and stay in L2).
   auto lora_phase = [&]() {
     if constexpr (EPI != EPI_LORA_T) {
       // The lane id passes through an empty asm here, so nothing derived from
@@ -262,18 +262,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
               for (int j = 0; j < NTL; ++j)
                 if (EPI != EPI_GATEUP || (j & 1) == SG) acc[i][j] = mfma32_f32(av, bf32[j], acc[i][j]);
             } else {
-              f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+              f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
               if (row < g.M) {
-                lo = *reinterpret_cast<const f32x4*>(tp);
-                hi = *reinterpret_cast<const f32x4*>(tp + 4);
+                t0 = *reinterpret_cast<const f32x4*>(tp);
+                t1 = *reinterpret_cast<const f32x4*>(tp + 4);
               }
-              const u32x4 af = u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                                     pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+              // t enters as two bf16 terms, its rounded value and the rounding
+              // residual, so the adapter adds no rounding point of its own
+              // (t is then carried to about 2^-17 relative).
+              const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+              uint32_t wh[4], wl[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                wh[q] = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
+                wl[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wh[q] << 16),
+                                    tv[2 * q + 1] - __uint_as_float(wh[q] & 0xffff0000u));
+              }
+              const u32x4 ah = u32x4{wh[0], wh[1], wh[2], wh[3]}, al = u32x4{wl[0], wl[1], wl[2], wl[3]};
 #pragma unroll
               for (int j = 0; j < NTL; ++j)
-                if (EPI != EPI_GATEUP || (j & 1) == SG)
-                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfr[j]),
+                if (EPI != EPI_GATEUP || (j & 1) == SG) {
+                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, bfr[j]),
                                           acc[i][j]);
+                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bfr[j]),
+                                          acc[i][j]);
+                }
             }
           }
         }

@@ -63,6 +63,12 @@ struct GemmArgs {
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
 hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st);
 
+// Adapter input of activation-space LoRA, bf16 operands: t[r][n] =
+// (accumulate ? t[r][n] : 0) + alpha * sum_k a[r][k] * w[n][k] for r < m,
+// n < rank (<= 256); k % 16 == 0, lda and ldw multiples of 8, 16-B aligned.
+hipError_t launch_lora_t(const void* a, int64_t lda, const void* w, int64_t ldw, int64_t m, int64_t k, int64_t rank,
+                         float alpha, int accumulate, float* t, int64_t ldt, hipStream_t st);
+
 // Optional QK RMSNorm (w: [head_dim] or null) and RoPE (cs/sn: [rows][ld_rope]
 // or null), in place on `rows` token rows of width d.
 hipError_t launch_qk_transform(int f32, void* x, int64_t ldx, int64_t rows, int d, int head_dim, const float* w,

@@ -117,10 +117,13 @@ def test_single_adapter_on_each_projection(shape, bar):
             assert max_abs(y, y_ref) <= 1e-4, name
         else:
             # alpha = 2 adapters make |y| reach 8 and more, where the output's own
-            # half-ulp is 0.016-0.03: the bar is 2e-2 beyond that half-ulp per
-            # element (the "rarer than 1e-4" count is meaningless on 16k elements)
+            # half-ulp is 0.016-0.03, and push the error of the path's own bf16
+            # rounding points past 2e-2 beyond that half-ulp (0.026 for the gate
+            # adapter in an fp64 emulation of those points: test_tolerance.py),
+            # so the bar per element is 3e-2 beyond the half-ulp (the "rarer than
+            # 1e-4" count is meaningless on 16k elements)
             assert rel_l2(y, y_ref) <= 1e-2, name
-            assert float((np.abs(y - y_ref) - half_ulp_bf16(y_ref)).max()) <= 2e-2, name
+            assert float((np.abs(y - y_ref) - half_ulp_bf16(y_ref)).max()) <= 3e-2, name
         assert rel_l2(y - y0, y_ref - y0_ref) <= bar, name
 
 
