@@ -42,6 +42,16 @@ TRAFFIC = {
         # Q slab + K + V^T + O, each bf16 [rows][5120]
         "algorithmic_bytes": (8192 + 32768 + 32768 + 8192) * 5120 * 2,
     },
+    "gate_up": {
+        "record": "gate_up_large_8192_traffic.json",
+        "kernel": "dit::gemm_kernel<unsigned short, unsigned short, 3,",
+        "sources": ["memory_bounded_chunked_amd/csrc/gemm.hip", "memory_bounded_chunked_amd/csrc/common.hpp",
+                    "memory_bounded_chunked_amd/csrc/kernels.hpp"],
+        "workload": "SwiGLU gate/up projection of one 8192-token slab: [8192 x 5120] x [2 x 13824 x 5120]^T "
+                    "-> h [8192 x 13824], bf16 (two launches: 256x256 and 256x128 tiles)",
+        # activations + gate/up weight rows + h, bf16
+        "algorithmic_bytes": (8192 * 5120 + 2 * 13824 * 5120 + 8192 * 13824) * 2,
+    },
     "final_layer": {
         "record": "final_layer_32k_traffic.json",
         "kernel": "dit::final_layer_kernel",
@@ -86,6 +96,12 @@ def traffic_probe(kind: str) -> int:
         vt = torch.randn(d, n, device=dev, generator=g).bfloat16()
         o = torch.empty(ca, d, device=dev, dtype=torch.bfloat16)
         run = lambda: B.attention(q, k, vt, o, h)  # noqa: E731
+    elif kind == "gate_up":
+        m, d, f = 8192, 5120, 13824
+        a_in = torch.randn(m, d, device=dev, generator=g).bfloat16()
+        w = (torch.randn(2 * f, d, device=dev, generator=g) / d ** 0.5).bfloat16()
+        h = torch.empty(m, f, device=dev, dtype=torch.bfloat16)
+        run = lambda: B.linear("bf16", "gateup", a_in, w, h, f, up_offset=f)  # noqa: E731
     else:
         n, d, od = FINAL_N, FINAL_D, FINAL_OUT
         x = torch.randn(n, d, device=dev, generator=g).bfloat16()
@@ -109,11 +125,16 @@ def record_traffic(kind: str, fetch_csv: str, write_csv: str) -> int:
     import csv
     spec = TRAFFIC[kind]
 
-    def last(path, key):
-        rows = [r for r in csv.DictReader(open(path)) if key in r["Kernel_Name"]]
-        return float(rows[-1]["Counter_Value"])
+    def rows_of(path, key):
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if key in r["Kernel_Name"]]
 
-    fk, wk = last(fetch_csv, spec["kernel"]), last(write_csv, spec["kernel"])
+    def total(path, key):  # one launch of the step: all dispatches of its kernel
+        return sum(rows_of(path, key))
+
+    def last(path, key):  # the copy kernel runs last
+        return rows_of(path, key)[-1]
+
+    fk, wk = total(fetch_csv, spec["kernel"]), total(write_csv, spec["kernel"])
     cf, cw = last(fetch_csv, "AUnaryFunctor"), last(write_csv, "AUnaryFunctor")
     fs, ws = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
     traffic = fk * 1024 * fs + wk * 1024 * ws
