@@ -97,6 +97,39 @@ def test_lora_ffn_feature_slices(case):
         check_bf16_bar(y, y_ref)
 
 
+@pytest.mark.parametrize("key", ["bf16", "f32", "w8_bf16"])
+def test_lora_with_qk_norm_rope_and_feature_slices(key):
+    # every widening of the block at once: adapters on all seven projections,
+    # QK RMSNorm + RoPE, and (in the second setting) FFN-feature slices
+    shape = SMALL[key]
+    inputs = synth.make_inputs(shape, 0)
+    qk_in = synth.make_qk_inputs(shape, 0)
+    lora = synth.make_lora(shape, RANKS, seed=2)
+    x, mod, w = oracle_inputs(inputs)
+    qk = {k: np.asarray(v, np.float64) for k, v in qk_in.items()}
+    y_ref = O.block_forward(x, mod, w, shape.n_heads, qk=qk, lora=_lora_f64(lora))
+    blk, xt, modt = B.block_from_inputs(shape, {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]})
+    blk.set_lora({k: (B.tensor_from_stored(a, "cuda"), B.tensor_from_stored(b, "cuda"), al)
+                  for k, (a, b, al) in lora.items()})
+    rope = (torch.from_numpy(qk_in["cos"]).cuda(), torch.from_numpy(qk_in["sin"]).cuda())
+    n = shape.n_tokens
+    outs = {}
+    for ca, cm, fc in ((256, 256, 0), (0, n, 0), (100, 300, 0), (256, 256, 128)):
+        xx = xt.clone()
+        blk.forward(xx, modt, ca, cm, fc, rope=rope)
+        torch.cuda.synchronize()
+        outs[(ca, cm, fc)] = xx.cpu()
+    blk.close()
+    base = outs[(256, 256, 0)]
+    assert all(bits(o) == bits(base) for k, o in outs.items() if k[2] == 0), "bit-identity across (Ca, Cm)"
+    for o in (base, outs[(256, 256, 128)]):
+        y = to_f64(o)
+        if shape.dtype == "f32":
+            assert max_abs(y, y_ref) <= 1e-4 and rel_l2(y, y_ref) <= 1e-4
+        else:
+            check_bf16_bar(y, y_ref)
+
+
 @pytest.mark.parametrize("shape,bar", [
     # fp32: the adapter's term is resolved to ~1e-6, so every target is held tightly
     (synth.BlockShape("single-f32", 256, 4, 64, 1024, 300, "f32"), 1e-3),
