@@ -7,21 +7,28 @@
 //
 //   out[t][j] = sum_c (LN(x[t])[c] * (1 + scale[c]) + shift[c]) * w[j][c]
 //
+// One pass over x. LayerNorm is linear in the row once its statistics are
+// known, so with a per-row shift p (the mean of the row's first 8 values),
+// u = x - p, g = 1 + scale:
+//
+//   out[t][j] = r * (S[j] - (mu - p) * C[j]) + B[j],
+//   S[j] = sum_c u[c] g[c] w[j][c],  C[j] = sum_c g[c] w[j][c],  B[j] = sum_c shift[c] w[j][c],
+//   mu - p = sum_c u[c] / d,  var = sum_c u[c]^2 / d - (mu - p)^2,  r = 1/sqrt(var + eps).
+//
+// The shift keeps the moments and S - (mu - p) C free of cancellation (p is
+// within a few standard deviations of the mean), and x is read from HBM once
+// instead of once for the statistics and again for the contraction.
+//
 // A workgroup owns 64 token rows (two 32x32 MFMA row tiles, which share every
 // weight fragment) and every output column (out_dim <= 128, i.e. up to 4
-// column tiles of 32).
-//   phase 1  each wave computes mean and 1/sqrt(var + eps) of 16 rows, two-pass
-//            over rows held in registers as stored (fp32 statistics), into LDS;
-//   phase 2  wave w contracts columns [w*d/4, (w+1)*d/4) of d: each lane loads
-//            8 consecutive x values of its row and normalises/modulates them in
-//            registers; those are the A operands of eight 32x32x2 fp32 MFMAs,
-//            whose B operands are 8 consecutive values of one w row. A and B use
-//            the same permutation of k inside a 16-column step, so the product
-//            is the plain contraction;
-//   reduce   the four waves' partial tiles are summed through LDS in the fixed
-//            order (w0 + w1) + (w2 + w3).
-// A 64-row tile (640 KB at d = 5120) does not stay on chip between the
-// statistics pass and the contraction, so x is fetched twice.
+// column tiles of 32). Wave w contracts columns [w*d/4, (w+1)*d/4) of d: each
+// lane loads 8 consecutive x values of its row, forms u g in registers (the A
+// operands of eight 32x32x2 fp32 MFMAs, whose B operands are 8 consecutive
+// values of one w row; A and B use the same permutation of k inside a
+// 16-column step, so the product is the plain contraction) and accumulates the
+// row's moments of u; the lanes that hold a w row accumulate C and B for it.
+// The four waves' partial tiles, moments and C/B are summed through LDS in the
+// fixed order (w0 + w1) + (w2 + w3), and the epilogue applies the formula.
 // The arithmetic of a row depends only on that row, d and out_dim: calling the
 // kernel on any range of rows gives the same bits for those rows.
 #include "common.hpp"
@@ -67,49 +74,6 @@ __device__ __forceinline__ void load8f(const float* p, float v[8]) {
   }
 }
 
-// Mean and 1/sqrt(var + eps) of R rows (two-pass over registers); lane 0
-// writes them to mu_out[q], rs_out[q].
-template <typename T, int G, int R>
-__device__ __forceinline__ void row_stats(const T* __restrict__ x, int64_t ldx, const int64_t (&rows)[R],
-                                          int ngroups, float inv_d, float eps, int lane, float* mu_out,
-                                          float* rs_out) {
-  Raw8<T> v[R][G];
-#pragma unroll
-  for (int q = 0; q < R; ++q) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int idx = g * 64 + lane;
-      if (idx < ngroups) v[q][g] = load_raw8(x + rows[q] * ldx + idx * 8);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < R; ++q) {
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (g * 64 + lane < ngroups) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s += raw_at(v[q][g], j);
-      }
-    const float mu = wave_sum(s) * inv_d;
-    float s2 = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (g * 64 + lane < ngroups) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float t = raw_at(v[q][g], j) - mu;
-          s2 += t * t;
-        }
-      }
-    const float var = wave_sum(s2) * inv_d;
-    if (lane == 0) {
-      mu_out[q] = mu;
-      rs_out[q] = 1.0f / sqrtf(var + eps);
-    }
-  }
-}
-
 template <typename T, int NT>
 struct FlStep {
   Raw8<T> xv[FL_BM / 32];
@@ -117,9 +81,8 @@ struct FlStep {
   float sc[8], sh[8];
 };
 
-// T: activation type of x (float or uint16_t = bf16). G: 8-column groups per
-// lane in phase 1 (d <= 512 * G). NT: 32-column output tiles.
-template <typename T, int G, int NT>
+// T: activation type of x (float or uint16_t = bf16). NT: 32-column output tiles.
+template <typename T, int NT>
 __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ x, int64_t ldx, int64_t n, int d,
                                                           const float* __restrict__ shift,
                                                           const float* __restrict__ scale,
@@ -127,39 +90,27 @@ __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ 
                                                           float* __restrict__ out, int64_t ldo, float eps) {
   constexpr int TW = NT * 32;  // padded tile width
   constexpr int MT = FL_BM / 32;
-  __shared__ float s_mu[FL_BM], s_rs[FL_BM];
   __shared__ float s_red[2][FL_BM][TW];
+  __shared__ float s_mom[FL_WAVES][FL_BM][2];  // per-wave sums of u and u^2 per row
+  __shared__ float s_cb[FL_WAVES][TW][2];      // per-wave partial C and B per column
+  __shared__ float s_dl[FL_BM], s_rs[FL_BM];   // mu - p and 1/sqrt(var + eps) per row
+  __shared__ float s_c[TW], s_b[TW];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, half = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * FL_BM;
 
-  // Phase 1: row statistics, FL_BM / 4 rows per wave, R rows in flight.
-  {
-    constexpr int R = (sizeof(T) == 2 && G <= 12) ? 2 : 1;
-    constexpr int PER_WAVE = FL_BM / FL_WAVES;
-    const int ngroups = d >> 3;
-    const float inv_d = 1.0f / (float)d;
-    for (int rr = 0; rr < PER_WAVE; rr += R) {
-      const int r = wave * PER_WAVE + rr;
-      int64_t rows[R];
-#pragma unroll
-      for (int q = 0; q < R; ++q) rows[q] = m0 + r + q < n ? m0 + r + q : n - 1;  // clamped rows unused
-      row_stats<T, G, R>(x, ldx, rows, ngroups, inv_d, eps, lane, s_mu + r, s_rs + r);
-    }
-  }
-  __syncthreads();
-
-  // Phase 2: this wave's quarter of the contraction for all MT row tiles.
-  const int lr = lane & 31, half = lane >> 5;
   const T* xr[MT];
-  float mu[MT], rs[MT];
+  float p[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int r = m * 32 + lr;
-    const int64_t row = m0 + r < n ? m0 + r : n - 1;  // clamped rows are computed and discarded
+    const int64_t row = m0 + m * 32 + lr < n ? m0 + m * 32 + lr : n - 1;  // clamped rows are computed and discarded
     xr[m] = x + row * ldx;
-    mu[m] = s_mu[r];
-    rs[m] = s_rs[r];
+    const Raw8<T> head = load_raw8(xr[m]);
+    float s8 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s8 += raw_at(head, i);
+    p[m] = s8 * 0.125f;
   }
   const float* wr[NT];
 #pragma unroll
@@ -172,6 +123,11 @@ __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ 
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f32x16{};
+  float s1[MT], s2[MT], cs[NT], bs[NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) s1[m] = s2[m] = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cs[t] = bs[t] = 0.f;
 
   auto fetch = [&](int k0, FlStep<T, NT>& s) {
     const int kk = k0 + 8 * half;
@@ -187,8 +143,16 @@ __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ 
     for (int i = 0; i < 8; ++i) {
       const float g = 1.0f + s.sc[i];
 #pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        cs[t] = fmaf(g, s.wv[t][i], cs[t]);
+        bs[t] = fmaf(s.sh[i], s.wv[t][i], bs[t]);
+      }
+#pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float a = (raw_at(s.xv[m], i) - mu[m]) * rs[m] * g + s.sh[i];
+        const float u = raw_at(s.xv[m], i) - p[m];
+        s1[m] += u;
+        s2[m] = fmaf(u, u, s2[m]);
+        const float a = u * g;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[m][t] = mfma32_f32(a, s.wv[t][i], acc[m][t]);
       }
@@ -209,7 +173,29 @@ __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ 
   }
   if (k0 < kend) compute(sa);
 
-  // Cross-wave reduction in the fixed order (w0 + w1) + (w2 + w3).
+  // Lanes l and l^32 hold the two halves of each 16-column step: combine them.
+  auto pair_sum = [](float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const float a1 = pair_sum(s1[m]), a2 = pair_sum(s2[m]);
+    if (half == 0) {
+      s_mom[wave][m * 32 + lr][0] = a1;
+      s_mom[wave][m * 32 + lr][1] = a2;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float c = pair_sum(cs[t]), b = pair_sum(bs[t]);
+    if (half == 0) {
+      s_cb[wave][t * 32 + lr][0] = c;
+      s_cb[wave][t * 32 + lr][1] = b;
+    }
+  }
+
+  // Cross-wave sums in the fixed order (w0 + w1) + (w2 + w3).
   auto put = [&](int buf, bool add) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -223,46 +209,36 @@ __global__ __launch_bounds__(256) void final_layer_kernel(const T* __restrict__ 
   };
   if ((wave & 1) == 0) put(wave >> 1, false);
   __syncthreads();
-  if (wave & 1) put(wave >> 1, true);
+  if (wave & 1) {
+    put(wave >> 1, true);
+  } else if (wave == 0) {  // row statistics, one row per lane
+    const float inv_d = 1.0f / (float)d;
+    const float u1 = (s_mom[0][lane][0] + s_mom[1][lane][0]) + (s_mom[2][lane][0] + s_mom[3][lane][0]);
+    const float u2 = (s_mom[0][lane][1] + s_mom[1][lane][1]) + (s_mom[2][lane][1] + s_mom[3][lane][1]);
+    const float dl = u1 * inv_d;
+    const float var = fmaxf(u2 * inv_d - dl * dl, 0.0f);
+    s_dl[lane] = dl;
+    s_rs[lane] = 1.0f / sqrtf(var + eps);
+  } else {  // wave 2: C and B per column
+    for (int c = lane; c < TW; c += 64) {
+      s_c[c] = (s_cb[0][c][0] + s_cb[1][c][0]) + (s_cb[2][c][0] + s_cb[3][c][0]);
+      s_b[c] = (s_cb[0][c][1] + s_cb[1][c][1]) + (s_cb[2][c][1] + s_cb[3][c][1]);
+    }
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < FL_BM * TW; e += 256) {
     const int r = e / TW, c = e % TW;
-    if (m0 + r < n && c < out_dim) out[(m0 + r) * ldo + c] = s_red[0][r][c] + s_red[1][r][c];
+    if (m0 + r < n && c < out_dim)
+      out[(m0 + r) * ldo + c] = s_rs[r] * ((s_red[0][r][c] + s_red[1][r][c]) - s_dl[r] * s_c[c]) + s_b[c];
   }
 }
 
 template <typename T, int NT>
 static hipError_t launch_fl_nt(const void* x, int64_t ldx, int64_t n, int d, const float* shift, const float* scale,
                                const float* w, int out_dim, float* out, int64_t ldo, float eps, hipStream_t st) {
-  const int g = (int)ceil_div(d / 8, 64);
   const dim3 grid((unsigned)ceil_div(n, FL_BM)), block(256);
-  const T* xx = static_cast<const T*>(x);
-#define DIT_FL_CASE(G)                                                                                     \
-  case G:                                                                                                  \
-    hipLaunchKernelGGL((final_layer_kernel<T, G, NT>), grid, block, 0, st, xx, ldx, n, d, shift, scale, w, \
-                       out_dim, out, ldo, eps);                                                            \
-    break;
-  switch (g) {
-    DIT_FL_CASE(1)
-    DIT_FL_CASE(2)
-    DIT_FL_CASE(3)
-    DIT_FL_CASE(4)
-    DIT_FL_CASE(5)
-    DIT_FL_CASE(6)
-    DIT_FL_CASE(7)
-    DIT_FL_CASE(8)
-    DIT_FL_CASE(9)
-    DIT_FL_CASE(10)
-    DIT_FL_CASE(11)
-    DIT_FL_CASE(12)
-    DIT_FL_CASE(13)
-    DIT_FL_CASE(14)
-    DIT_FL_CASE(15)
-    DIT_FL_CASE(16)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef DIT_FL_CASE
+  hipLaunchKernelGGL((final_layer_kernel<T, NT>), grid, block, 0, st, static_cast<const T*>(x), ldx, n, d, shift,
+                     scale, w, out_dim, out, ldo, eps);
   return hipGetLastError();
 }
 
