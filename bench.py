@@ -149,7 +149,7 @@ def record_traffic(kind: str, fetch_csv: str, write_csv: str) -> int:
         "fetch_scale": fs, "write_scale": ws,
         "traffic_bytes_per_launch": traffic,
         "algorithmic_bytes_per_launch": spec["algorithmic_bytes"],
-        "commands": [f"TMPDIR=/tmp rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic_{kind}_{c} -o t "
+        "commands": [f"TMPDIR=/tmp rocprofv3 --pmc {c} --output-format csv -d traffic_{kind}_{c} -o t "
                      f"-- python3 bench.py --probe {kind}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
                     + [f"python3 bench.py --record-traffic {kind} <FETCH_SIZE counter_collection.csv> "
                        f"<WRITE_SIZE counter_collection.csv>"],
@@ -253,7 +253,7 @@ def bench_final_layer(args) -> int:
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded PCG64 inputs; see DESIGN.md recipe)",
+        "data": "synthetic (seeded PCG64 inputs at the workload's shapes)",
         "config": {"workload": f"DiT output head: N={n} bf16 token rows, d={d} -> {od} fp32 outputs, batch 1",
                    "n_tokens": n, "d": d, "out_dim": od, "workspace_bytes": 0},
         "roofline": {"kernel": "final_layer", "bound": "mfma", "achieved": round(achieved, 2),
@@ -412,7 +412,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "w8_bf16": "w8a16-bf16"}[shape.dtype],
-        "data": "synthetic (seeded PCG64 inputs; see DESIGN.md recipe)",
+        "data": "synthetic (seeded PCG64 inputs at the workload's shapes)",
         "config": {
             "workload": (f"{shape.name} DiT block forward: d={d}, {shape.n_heads}x{shape.head_dim} heads, "
                          f"SwiGLU F={shape.ffn}, N={n} tokens, batch 1"
