@@ -239,57 +239,61 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
         constexpr int KS = A_F32 ? 2 : 16;  // k per MFMA
         const int64_t r = g.lora_r[SG];
         const TA* bbase = static_cast<const TA*>(g.lora_b[SG]);
-        for (int64_t k0 = 0; k0 < r; k0 += KS) {
-          const int64_t kk = g.lora_toff[SG] + k0 + (A_F32 ? hf : 8 * hf);
-          u32x4 bfr[NTL];
-          float bf32[NTL];
+        // bf16: t enters as two bf16 terms, its rounded value (first sweep)
+        // and the rounding residual (second sweep), so the adapter adds no
+        // rounding point of its own (t is carried to about 2^-17 relative).
+        // One term per sweep keeps few registers live.
+        auto sweep = [&](auto part_c) {
+          constexpr int PART = decltype(part_c)::value;
+          for (int64_t k0 = 0; k0 < r; k0 += KS) {
+            const int64_t kk = g.lora_toff[SG] + k0 + (A_F32 ? hf : 8 * hf);
+            u32x4 bfr[NTL];
+            float bf32[NTL];
 #pragma unroll
-          for (int j = 0; j < NTL; ++j) {
-            if (EPI == EPI_GATEUP && (j & 1) != SG) continue;
-            const TA* bp = bbase + brow[j] * r + k0;
-            if constexpr (A_F32)
-              bf32[j] = load_act(bp + hf);
-            else
-              bfr[j] = *reinterpret_cast<const u32x4*>(bp + 8 * hf);
-          }
+            for (int j = 0; j < NTL; ++j) {
+              if (EPI == EPI_GATEUP && (j & 1) != SG) continue;
+              const TA* bp = bbase + brow[j] * r + k0;
+              if constexpr (A_F32)
+                bf32[j] = load_act(bp + hf);
+              else
+                bfr[j] = *reinterpret_cast<const u32x4*>(bp + 8 * hf);
+            }
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const int64_t row = m0 + wm * WTM + i * 32 + l32;
-            const float* tp = g.lora_t + (row < g.M ? row : 0) * g.lora_ldt + kk;
-            if constexpr (A_F32) {
-              const float av = row < g.M ? *tp : 0.f;
+            for (int i = 0; i < MT; ++i) {
+              const int64_t row = m0 + wm * WTM + i * 32 + l32;
+              const float* tp = g.lora_t + (row < g.M ? row : 0) * g.lora_ldt + kk;
+              if constexpr (A_F32) {
+                const float av = row < g.M ? *tp : 0.f;
 #pragma unroll
-              for (int j = 0; j < NTL; ++j)
-                if (EPI != EPI_GATEUP || (j & 1) == SG) acc[i][j] = mfma32_f32(av, bf32[j], acc[i][j]);
-            } else {
-              f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
-              if (row < g.M) {
-                t0 = *reinterpret_cast<const f32x4*>(tp);
-                t1 = *reinterpret_cast<const f32x4*>(tp + 4);
-              }
-              // t enters as two bf16 terms, its rounded value and the rounding
-              // residual, so the adapter adds no rounding point of its own
-              // (t is then carried to about 2^-17 relative).
-              const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-              uint32_t wh[4], wl[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                wh[q] = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
-                wl[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wh[q] << 16),
-                                    tv[2 * q + 1] - __uint_as_float(wh[q] & 0xffff0000u));
-              }
-              const u32x4 ah = u32x4{wh[0], wh[1], wh[2], wh[3]}, al = u32x4{wl[0], wl[1], wl[2], wl[3]};
-#pragma unroll
-              for (int j = 0; j < NTL; ++j)
-                if (EPI != EPI_GATEUP || (j & 1) == SG) {
-                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, bfr[j]),
-                                          acc[i][j]);
-                  acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bfr[j]),
-                                          acc[i][j]);
+                for (int j = 0; j < NTL; ++j)
+                  if (EPI != EPI_GATEUP || (j & 1) == SG) acc[i][j] = mfma32_f32(av, bf32[j], acc[i][j]);
+              } else {
+                f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
+                if (row < g.M) {
+                  t0 = *reinterpret_cast<const f32x4*>(tp);
+                  t1 = *reinterpret_cast<const f32x4*>(tp + 4);
                 }
+                const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+                uint32_t wv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  wv[q] = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
+                  if constexpr (PART == 1)
+                    wv[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wv[q] << 16),
+                                        tv[2 * q + 1] - __uint_as_float(wv[q] & 0xffff0000u));
+                }
+                const u32x4 af = u32x4{wv[0], wv[1], wv[2], wv[3]};
+#pragma unroll
+                for (int j = 0; j < NTL; ++j)
+                  if (EPI != EPI_GATEUP || (j & 1) == SG)
+                    acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfr[j]),
+                                            acc[i][j]);
+              }
             }
           }
-        }
+        };
+        sweep(std::integral_constant<int, 0>{});
+        if constexpr (!A_F32) sweep(std::integral_constant<int, 1>{});
       };
       if constexpr (EPI == EPI_GATEUP) {
         lora_seg(std::integral_constant<int, 0>{});
