@@ -1,0 +1,61 @@
+"""Register allocation of the built library (CPU): no kernel spills VGPRs to
+scratch, except the two int8-weight 256x256 GEMM kernels (gate/up and K|V),
+whose adapter phase runs after the main loop with all accumulators live.
+A spill inside a hot loop costs far more than it looks (scratch traffic goes
+through L2 and shows up as HBM fetches), so any new spill fails here.
+
+Reads the AMDGPU metadata notes of the gfx950 code objects embedded in
+libdit_block.so, with the LLVM tools of the ROCm install.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "memory_bounded_chunked_amd", "libdit_block.so")
+LLVM = "/opt/rocm/llvm/bin"
+ALLOWED = {
+    "_ZN3dit11gemm_kernelItaLi3ELi256ELi256ELi2ELi4EEEvNS_8GemmArgsE",  # int8 gate/up, adapter phase
+    "_ZN3dit11gemm_kernelItaLi6ELi256ELi256ELi2ELi4EEEvNS_8GemmArgsE",  # int8 K|V, adapter phase
+}
+
+
+def _kernels(tmp_path):
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    for tool in ("clang-offload-bundler", "llvm-readelf"):
+        if not os.path.exists(os.path.join(LLVM, tool)):
+            pytest.skip(f"{tool} not available")
+    objcopy = shutil.which("objcopy")
+    if objcopy is None:
+        pytest.skip("objcopy not available")
+    fat = tmp_path / "fatbin.bin"
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", LIB, str(tmp_path / "lib.so")], check=True)
+    data = fat.read_bytes()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+    kernels = {}
+    for i, s in enumerate(starts):
+        e = starts[i + 1] if i + 1 < len(starts) else len(data)
+        b, co = tmp_path / f"b{i}.bin", tmp_path / f"co{i}.o"
+        b.write_bytes(data[s:e])
+        subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={b}", f"--output={co}"], check=True)
+        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", str(co)], check=True,
+                               capture_output=True, text=True).stdout
+        names = re.findall(r"^\s+\.name:\s+(\S+)", notes, re.M)
+        spills = re.findall(r"^\s+\.vgpr_spill_count:\s+(\d+)", notes, re.M)
+        assert len(names) == len(spills)
+        kernels.update(zip(names, map(int, spills)))
+    return kernels
+
+
+def test_no_vgpr_spills(tmp_path):
+    kernels = _kernels(tmp_path)
+    assert any("attention_bf16_kernel" in k for k in kernels)
+    assert any("lora_t_kernel" in k for k in kernels)
+    spilling = {k: v for k, v in kernels.items() if v and k not in ALLOWED}
+    assert not spilling, spilling
