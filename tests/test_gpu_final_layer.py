@@ -105,6 +105,24 @@ def test_final_layer_constant_rows():
     assert max_abs(out, np.broadcast_to(expect, out.shape)) <= 1e-5
 
 
+def test_final_layer_rows_far_from_zero_mean():
+    # The kernel takes the moments of x - p for a per-row shift p (the mean of
+    # the row's first 8 values): rows centred far from zero, some with an
+    # outlier among those first values, must still match the oracle.
+    n, d, out_dim = 96, 1024, 64
+    inp = synth.make_final_inputs(n, d, out_dim, "f32", seed=4)
+    x = inp["x"].astype(np.float64)
+    x = 1000.0 + x
+    x[::3, 0] += 50.0
+    x[1::3, :8] -= 20.0
+    inp["x"] = x.astype(np.float32)
+    t = _device(inp)
+    got = B.final_layer(t["x"], t["shift"], t["scale"], t["w_out"]).cpu().numpy().astype(np.float64)
+    ref = _oracle(inp)
+    assert max_abs(got, ref) <= 1e-4 * max(1.0, float(np.abs(ref).max()))
+    assert rel_l2(got, ref) <= 1e-4
+
+
 def test_final_layer_full_size_sampled_rows():
     n, d, out_dim = 32768, 5120, 64
     print(f"final_layer full n={n} d={d} out_dim={out_dim}", flush=True)
