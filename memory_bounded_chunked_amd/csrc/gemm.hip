@@ -26,6 +26,7 @@
 // Weight-only int8 (W8_BF16): B is int8 in HBM and is widened exactly to bf16
 // on its way into LDS (|q| <= 127 needs 7 significant bits); the per-row scale
 // multiplies the fp32 accumulator in the epilogue.
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -503,17 +504,18 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent callers
+// may both query, and store the same value).
 static int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Column split between 256-wide B tiles (wb output columns each: 256, or 128
