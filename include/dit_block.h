@@ -135,7 +135,10 @@ int dit_block_plan_chunks(const dit_block* h, int64_t n_tokens, size_t budget_by
  *   x          [N][d] activations (fp32 for F32, else bf16), read and
  *              overwritten with the block output y. 16-byte aligned.
  *   mod        [6][d] fp32: shift1, scale1, gate1, shift2, scale2, gate2.
- *   n_tokens   N >= 1.
+ *   n_tokens   N >= 1, and head_dim * Np * e < 2^32 (Np = N rounded up to
+ *              64, e = activation bytes): the attention kernel addresses a
+ *              head's rows of the transposed V with 32-bit offsets (N below
+ *              16.7 M tokens for bf16 at head_dim 128); larger N is DIT_EINVAL.
  *   attn_chunk_tokens   query tokens per attention slice (>= 0; 0 = one slice
  *              of all N tokens, the pages' "stock attention" setting).
  *   mlp_chunk_tokens    tokens per MLP slice (>= 1).

@@ -41,7 +41,8 @@ int dit_modnorm(int32_t in_dtype, int32_t out_dtype, const void* x, int64_t ldx,
  * q: [n_q][ldq], k: [n_kv][ldk], o: [n_q][ldo]; vt: V transposed,
  * [n_heads*head_dim][ldvt] (row c holds column c of V for all keys).
  * dtype DIT_F32 or DIT_BF16 (fp32 softmax, bf16 P and O for DIT_BF16).
- * head_dim 64 or 128; ldq, ldk, ldo >= n_heads*head_dim; ldvt >= n_kv;
+ * head_dim 64 or 128; ldq, ldk, ldo >= n_heads*head_dim; ldvt >= n_kv and
+ * head_dim * ldvt * (element bytes) < 2^32 (32-bit offsets within a head's V^T rows);
  * all leading dimensions multiples of 8. n_q == 0 enqueues nothing. */
 int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
                   const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv,

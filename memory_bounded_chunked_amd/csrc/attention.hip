@@ -635,6 +635,8 @@ hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k
                             int64_t n_kv, int n_heads, int head_dim, hipStream_t st) {
   if (n_q <= 0) return hipSuccess;
   if (n_kv <= 0) return hipErrorInvalidValue;
+  // per-thread offsets into a V^T tile are 32-bit: head_dim rows of ldvt elements
+  if ((int64_t)head_dim * ldvt * (dtype == F32 ? 4 : 2) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
   if (dtype == F32) {
     if (head_dim == 64) return launch_att_t<float, 64, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
     if (head_dim == 128) return launch_att_t<float, 128, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);

@@ -72,6 +72,8 @@ int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chu
   p->fc = ffn_chunk == 0 ? f : std::min(ffn_chunk, f);
   p->s = std::max(p->ca, p->cm);
   p->np = (n + 63) / 64 * 64;
+  // the attention kernel addresses a head's V^T rows with 32-bit offsets
+  if (h->desc.head_dim * p->np * e >= ((int64_t)1 << 32)) return DIT_EINVAL;
   const size_t k_bytes = round_up((size_t)n * d * e, kAlign);
   const size_t vt_bytes = round_up((size_t)d * p->np * e, kAlign);
   const size_t stage_bytes = round_up((size_t)p->s * d * 4, kAlign);
@@ -553,6 +555,7 @@ int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int6
   const int64_t d = n_heads * head_dim;
   if (ldq < d || ldk < d || ldo < d || ldvt < n_kv) return DIT_EINVAL;
   if (ldq % 8 || ldk % 8 || ldo % 8 || ldvt % 8) return DIT_EINVAL;
+  if (head_dim * ldvt * (dtype == DIT_F32 ? 4 : 2) >= ((int64_t)1 << 32)) return DIT_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return DIT_EINVAL;
   if (n_q == 0) return DIT_OK;
   return hip_status(dit::launch_attention(dtype, q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, (int)n_heads,

@@ -83,6 +83,17 @@ def test_workspace_closed_form(lib, n, ca, cm, fc):
         lib.dit_block_destroy(h)
 
 
+def test_token_count_limit_of_the_attention_offsets(lib):
+    # bf16, head_dim 128: 128 * Np * 2 bytes must stay below 2^32
+    rc, h = _handle(lib)
+    assert rc == B.DIT_OK
+    try:
+        assert _ws(lib, h, (1 << 24) - 64, 256, 256, 0)[0] == B.DIT_OK
+        assert _ws(lib, h, (1 << 24) - 63, 256, 256, 0)[0] == B.DIT_EINVAL
+    finally:
+        lib.dit_block_destroy(h)
+
+
 def test_workspace_figures_at_32k():
     # headline block (d=5120, F=13824, N=32768, chunks 8192/8192): K,V 640 MiB,
     # fp32 staging 160 MiB, slabs max(160, 296) MiB -> 1096 MiB; only K/V grow with N
@@ -129,6 +140,10 @@ def test_step_entry_points_reject_before_launch(lib):
     assert lib.dit_attention(1, p, 256, p, 256, p, 104, p, 256, 10, 100, 2, 96, None) == B.DIT_EINVAL
     assert lib.dit_attention(2, p, 256, p, 256, p, 104, p, 256, 10, 100, 2, 128, None) == B.DIT_EINVAL
     assert lib.dit_attention(1, p, 256, p, 256, p, 104, p, 256, 0, 100, 2, 128, None) == B.DIT_OK
+    # 32-bit offsets within a head's V^T rows: head_dim * ldvt * element bytes < 2^32
+    assert lib.dit_attention(1, p, 256, p, 256, p, 1 << 24, p, 256, 0, 100, 2, 128, None) == B.DIT_EINVAL
+    assert lib.dit_attention(1, p, 256, p, 256, p, (1 << 24) - 8, p, 256, 0, 100, 2, 128, None) == B.DIT_OK
+    assert lib.dit_attention(0, p, 256, p, 256, p, 1 << 23, p, 256, 0, 100, 2, 128, None) == B.DIT_EINVAL
     # dit_linear: k not a multiple of 64, n not a multiple of 64, int8 without scale, missing gate
     assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 10, 256, 100, p, 256, None, 0, None, None) == B.DIT_EINVAL
     assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 10, 200, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
