@@ -93,7 +93,9 @@ typedef struct dit_block_weights {
  * only host metadata (no device calls). *out is set on success.
  * Errors: DIT_EINVAL for a null pointer, d != n_heads*head_dim, head_dim not
  * in {64,128}, ffn < 64 or not a multiple of 64, an unknown dtype, eps <= 0,
- * a weight pointer not 16-byte aligned, or a missing W8 scale. */
+ * a weight pointer not 16-byte aligned, or a missing W8 scale; also when
+ * (ffn + 256) * d or 256 * ffn weight or activation elements reach 2^32 bytes
+ * (the projections address one tile's rows with 32-bit byte offsets). */
 int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit_block** out);
 
 /* Exact workspace bytes that dit_block_forward needs for these arguments

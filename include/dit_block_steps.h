@@ -83,7 +83,10 @@ int dit_qk_transform(int32_t dtype, void* x, int64_t ldx, int64_t rows, int64_t 
  *   out: [m][ldo] (or [n][ldo] for DIT_EPI_STORE_T); aux: [m][ldaux];
  *   gate: [n] fp32 (RESID, ACCUM, FINAL).
  * k % 64 == 0 (k % 32 for DIT_F32); n % 64 == 0; leading dims multiples of 8
- * (of 16 for int8 weights). m == 0 enqueues nothing. */
+ * (of 16 for int8 weights). The kernel reaches the rows of one 256-row tile
+ * through 32-bit byte offsets, so 256 * lda * (activation bytes) and
+ * R * ldw * (weight bytes) must stay below 2^32, with R = up_offset + 256 for
+ * DIT_EPI_GATEUP and 256 otherwise; else DIT_EINVAL. m == 0 enqueues nothing. */
 int dit_linear(int32_t dtype, int32_t epilogue, const void* a, int64_t lda, const void* w,
                int64_t ldw, const float* w_scale, int64_t up_offset, int64_t m, int64_t n,
                int64_t k, void* out, int64_t ldo, const void* aux, int64_t ldaux,

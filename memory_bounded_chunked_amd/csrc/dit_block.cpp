@@ -156,6 +156,10 @@ int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit
   if (d.n_heads < 1 || d.d != d.n_heads * d.head_dim || d.d > 8192) return DIT_EINVAL;
   if (d.ffn < 64 || d.ffn % 64) return DIT_EINVAL;
   if (!(d.eps > 0.f)) return DIT_EINVAL;
+  // the projection kernels address a tile's weight rows with 32-bit offsets
+  if (!dit::gemm_offsets_fit(d.dtype, d.d, d.d, d.ffn + 256) ||
+      !dit::gemm_offsets_fit(d.dtype, d.ffn, d.ffn, 256))
+    return DIT_EINVAL;
   const void* ptrs[4] = {w->w_qkv, w->w_o, w->w_gu, w->w_down};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return DIT_EINVAL;
@@ -578,6 +582,8 @@ int dit_linear(int32_t dtype, int32_t epilogue, const void* a, int64_t lda, cons
   if (epilogue == DIT_EPI_GATEUP && up_offset < n) return DIT_EINVAL;
   if (epilogue == DIT_EPI_STORE_T ? ldo < m : ldo < n) return DIT_EINVAL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(out) || (aux && !aligned16(aux))) return DIT_EINVAL;
+  if (!dit::gemm_offsets_fit(dtype, lda, ldw, epilogue == DIT_EPI_GATEUP ? up_offset + 256 : 256))
+    return DIT_EINVAL;
   if (m == 0) return DIT_OK;
   dit::GemmArgs g{};
   g.a = a;

@@ -595,6 +595,8 @@ hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g_in, hipStream_
   GemmArgs g = g_in;
   g.col0 = 0;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (!gemm_offsets_fit(dtype, g.lda, g.ldb, epi == EPI_GATEUP ? g.up_offset + 256 : 256))
+    return hipErrorInvalidValue;
   const int bk = dtype == F32 ? 32 : 64;
   if (g.K <= 0 || g.K % bk) return hipErrorInvalidValue;
   switch (dtype) {

@@ -63,6 +63,16 @@ struct GemmArgs {
 // dtype: 0 = F32, 1 = BF16, 2 = W8_BF16 (activations bf16, weights int8).
 hipError_t launch_gemm(int dtype, Epilogue epi, const GemmArgs& g, hipStream_t st);
 
+// The GEMM kernel reaches the rows of one tile through 32-bit byte offsets
+// from the tile's first row: 256 rows of A (leading dimension lda) and
+// b_rows_span rows of B (256, or up_offset + 256 for gate/up pairs). True when
+// both stay below 2^32 bytes.
+inline bool gemm_offsets_fit(int dtype, int64_t lda, int64_t ldb, int64_t b_rows_span) {
+  const int64_t ea = dtype == 0 ? 4 : 2, eb = dtype == 0 ? 4 : (dtype == 1 ? 2 : 1);
+  const int64_t lim = (int64_t)1 << 32;
+  return 256 * lda * ea < lim && b_rows_span * ldb * eb < lim;
+}
+
 // Adapter input of activation-space LoRA, bf16 operands: t[r][n] =
 // (accumulate ? t[r][n] : 0) + alpha * sum_k a[r][k] * w[n][k] for r < m,
 // n < rank (<= 256); k % 16 == 0, lda and ldw multiples of 8, 16-B aligned.

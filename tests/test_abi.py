@@ -94,6 +94,19 @@ def test_token_count_limit_of_the_attention_offsets(lib):
         lib.dit_block_destroy(h)
 
 
+def test_weight_size_limit_of_the_projection_offsets(lib):
+    # one gate/up tile spans rows f .. f + F + 255 of the [2F][d] weight, addressed
+    # with 32-bit byte offsets: (F + 256) * d * (weight bytes) must stay below 2^32
+    for dtype, wb in ((1, 2), (0, 4), (2, 1)):
+        f_max = (1 << 32) // (8192 * wb) - 256  # first F whose span reaches 2^32
+        f_ok = f_max - 64 if f_max % 64 == 0 else f_max // 64 * 64
+        rc, h = _handle(lib, d=8192, heads=64, ffn=f_ok, dtype=dtype)
+        assert rc == B.DIT_OK, (dtype, f_ok)
+        lib.dit_block_destroy(h)
+        rc, _ = _handle(lib, d=8192, heads=64, ffn=(f_max + 63) // 64 * 64, dtype=dtype)
+        assert rc == B.DIT_EINVAL, dtype
+
+
 def test_workspace_figures_at_32k():
     # headline block (d=5120, F=13824, N=32768, chunks 8192/8192): K,V 640 MiB,
     # fp32 staging 160 MiB, slabs max(160, 296) MiB -> 1096 MiB; only K/V grow with N
@@ -151,6 +164,15 @@ def test_step_entry_points_reject_before_launch(lib):
     assert lib.dit_linear(1, 2, p, 256, p, 256, None, 0, 10, 256, 256, p, 256, p, 256, None, None) == B.DIT_EINVAL
     assert lib.dit_linear(1, 3, p, 256, p, 256, None, 100, 10, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
     assert lib.dit_linear(1, 0, p, 256, p, 256, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+    # dit_linear: 32-bit tile offsets, 256 * lda * 2 and R * ldw * (weight bytes) below 2^32
+    big = 1 << 23
+    assert lib.dit_linear(1, 0, p, big - 8, p, 256, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+    assert lib.dit_linear(1, 0, p, big, p, 256, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(1, 0, p, 256, p, big, None, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
+    assert lib.dit_linear(2, 0, p, 256, p, big, p, 0, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+    up = (1 << 32) // (8192 * 2) - 256  # gate/up span (up_offset + 256) rows of 8192 bf16
+    assert lib.dit_linear(1, 3, p, 8192, p, 8192, None, up - 8, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_OK
+    assert lib.dit_linear(1, 3, p, 8192, p, 8192, None, up, 0, 256, 256, p, 256, None, 0, None, None) == B.DIT_EINVAL
 
 
 def test_final_layer_rejects_before_launch(lib):
