@@ -6,6 +6,9 @@
 // buffered: the next k-tile's global loads are in flight while the current
 // one is multiplied); WM x WN wavefronts (8 for BN = 256 or 128: two per
 // SIMD) each compute a (256/WM) x (BN/WN) block with accumulators in VGPRs.
+// With 8 waves and bf16 activations the two waves of each SIMD run one
+// phase apart (the two-group schedule at the main loop), so one multiplies
+// while the other reads LDS.
 // LDS rows hold 128 B of k and are padded to 144 B:
 // consecutive rows start 4 banks apart, so fragment reads are conflict-free
 // and their addresses are a per-lane base plus compile-time offsets.
@@ -130,14 +133,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 
   // Global loads: a uniform base advanced per k-tile plus a 32-bit byte
   // offset per thread and chunk (row * ld + chunk), fixed for the whole loop.
+  // Tile rows past the last token row load that last row again: an output
+  // row depends only on its own A row, and rows past M are never stored, so
+  // the loads need no branch (which also lets the compiler count them exactly
+  // when it waits for them).
   uint32_t aoff[A_LD], boff[B_LD];
-  bool aval[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int c = tid + i * NTHR;
-    const int64_t gr = m0 + (c >> 3);
-    aval[i] = gr < g.M;
-    aoff[i] = aval[i] ? (uint32_t)((gr - m0) * g.lda * (int64_t)sizeof(TA) + (c & 7) * 16) : 0u;
+    const int64_t gr = m0 + (c >> 3) < g.M ? m0 + (c >> 3) : g.M - 1;
+    aoff[i] = (uint32_t)((gr - m0) * g.lda * (int64_t)sizeof(TA) + (c & 7) * 16);
   }
   const int64_t b_first = b_row(0);
   bool bval[B_LD];  // EPI_LORA_T: B rows past n_valid read as zero
@@ -154,24 +159,32 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // One register staging set: tile kt+1 is written from it to LDS while
   // tile kt is multiplied, then it is refilled with tile kt+2 (see below).
   u32x4 ra[A_LD], rb[B_LD];
-  auto load_tiles = [&](int64_t k0) {
+  auto load_a = [&](int64_t k0) {
     const char* at = a_base + k0 * (int64_t)sizeof(TA);
-    const char* bt = b_base + k0 * (int64_t)sizeof(TB);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
-      ra[i] = aval[i] ? *reinterpret_cast<const u32x4*>(at + aoff[i]) : u32x4{0u, 0u, 0u, 0u};
+      ra[i] = *reinterpret_cast<const u32x4*>(at + aoff[i]);
+  };
+  auto load_b = [&](int64_t k0) {
+    const char* bt = b_base + k0 * (int64_t)sizeof(TB);
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
       rb[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bt + boff[i]) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto store_tiles = [&](int buf) {
+  auto load_tiles = [&](int64_t k0) {
+    load_a(k0);
+    load_b(k0);
+  };
+  auto store_a = [&](int buf) {
     char* As = smem + buf * STAGE;
-    char* Bs = As + BM * LDS_ROW;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int c = tid + i * NTHR;
       *reinterpret_cast<u32x4*>(As + lds_slot(c >> 3, c & 7)) = ra[i];
     }
+  };
+  auto store_b = [&](int buf) {
+    char* Bs = smem + buf * STAGE + BM * LDS_ROW;
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int c = tid + i * NTHR;
@@ -185,6 +198,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
         *reinterpret_cast<u32x4*>(Bs + lds_slot(r, ch)) = rb[i];
       }
     }
+  };
+  auto store_tiles = [&](int buf) {
+    store_a(buf);
+    store_b(buf);
   };
 
   f32x16 acc[MT][NTL];
@@ -311,6 +328,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   };
 
   const int a_rd = lds_slot(arow, half), b_rd = lds_slot(brow, half);
+  // Fragments of k-steps s0 and s0+1 of the tile in LDS buffer buf, and
+  // their MFMAs (for each accumulator, k-step s0 before s0+1).
+  auto read_frags = [&](int buf, int s0, u32x4 (&af)[2][MT], u32x4 (&bfr)[2][NTL]) {
+    const char* As = smem + buf * STAGE + a_rd;
+    const char* Bs = smem + buf * STAGE + BM * LDS_ROW + b_rd;
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        af[ss][i] = *reinterpret_cast<const u32x4*>(As + i * 32 * LDS_ROW + (s0 + ss) * 32);
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+        bfr[ss][j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * LDS_ROW + (s0 + ss) * 32);
+    }
+  };
+  auto mfma_frags = [&](const u32x4 (&af)[2][MT], const u32x4 (&bfr)[2][NTL]) {
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+          acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af[ss][i]), __builtin_bit_cast(bf16x8, bfr[ss][j]),
+                                  acc[i][j]);
+  };
   auto compute = [&](int buf) {
     const char* As = smem + buf * STAGE + a_rd;
     const char* Bs = smem + buf * STAGE + BM * LDS_ROW + b_rd;
@@ -352,20 +394,68 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   store_tiles(0);
   if (KT > 1) load_tiles(BK);
   __syncthreads();
+  // Two-group schedule for 8 waves (bf16 activations). Waves 0-3 and 4-7 each
+  // hold one wave per SIMD, and group 1 runs one phase behind group 0, so on
+  // every SIMD one wave issues MFMAs while the other reads its next
+  // fragments from LDS and moves the next tile in. A k-tile is four phases,
+  // each closed by a workgroup barrier:
+  //   M1: read fragments of k-steps 0-1; store A of tile kt+1 into the other
+  //       buffer, then load A of tile kt+2 into the staging registers
+  //   C1: MFMAs of k-steps 0-1
+  //   M2: read fragments of k-steps 2-3; store B of tile kt+1, load B of kt+2
+  //   C2: MFMAs of k-steps 2-3
+  // Tile kt+1 is complete in LDS (both groups' stores) before either group
+  // reads it, and the buffer it overwrites was last read (tile kt-1) before
+  // the barrier that opens the first store; the barriers count the same for
+  // both groups (group 1 takes one more before the loop, group 0 one more
+  // after it). Each accumulator still takes k-steps 0, 1, 2, 3 of each tile in
+  // order, as in the one-group schedule.
+  constexpr bool PP = !A_F32 && WM * WN == 8;
   int kt = 0;
-  for (; kt + 2 < KT; ++kt) {
+  if constexpr (PP) {
+    const int grp = wave >> 2;
+    auto phase_end = []() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (grp == 1) phase_end();
+    u32x4 af[2][MT], bfr[2][NTL];
+    // The last two iterations reload the last k-tile and store it into the
+    // buffer no later phase reads, so every iteration has the same shape.
+    const int64_t k_last = (int64_t)(KT - 1) * BK;
+    for (; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      const int64_t k_next2 = (int64_t)(kt + 2) * BK < k_last ? (int64_t)(kt + 2) * BK : k_last;
+      read_frags(cur, 0, af, bfr);
+      store_a(cur ^ 1);
+      load_a(k_next2);
+      phase_end();
+      mfma_frags(af, bfr);
+      phase_end();
+      read_frags(cur, 2, af, bfr);
+      store_b(cur ^ 1);
+      load_b(k_next2);
+      phase_end();
+      mfma_frags(af, bfr);
+      phase_end();
+    }
+    if (grp == 0) phase_end();
+  } else {
+    for (; kt + 2 < KT; ++kt) {
+      compute(kt & 1);
+      store_tiles((kt + 1) & 1);
+      load_tiles((int64_t)(kt + 2) * BK);
+      __syncthreads();
+    }
+    if (kt + 1 < KT) {
+      compute(kt & 1);
+      store_tiles((kt + 1) & 1);
+      __syncthreads();
+      ++kt;
+    }
     compute(kt & 1);
-    store_tiles((kt + 1) & 1);
-    load_tiles((int64_t)(kt + 2) * BK);
-    __syncthreads();
   }
-  if (kt + 1 < KT) {
-    compute(kt & 1);
-    store_tiles((kt + 1) & 1);
-    __syncthreads();
-    ++kt;
-  }
-  compute(kt & 1);
 
   // int8 weights: the adapter term joins after the contraction and the
   // per-row scale (which belongs to W a only) is applied before it.
