@@ -43,7 +43,10 @@ int dit_modnorm(int32_t in_dtype, int32_t out_dtype, const void* x, int64_t ldx,
  * dtype DIT_F32 or DIT_BF16 (fp32 softmax, bf16 P and O for DIT_BF16).
  * head_dim 64 or 128; ldq, ldk, ldo >= n_heads*head_dim; ldvt >= n_kv and
  * head_dim * ldvt * (element bytes) < 2^32 (32-bit offsets within a head's V^T rows);
- * all leading dimensions multiples of 8. n_q == 0 enqueues nothing. */
+ * all leading dimensions multiples of 8. The bf16 kernel may read V^T
+ * columns n_kv .. (n_kv rounded up to 8) - 1 (inside each row, since ldvt is
+ * a multiple of 8) and never lets their values reach o, whatever they hold.
+ * n_q == 0 enqueues nothing. */
 int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
                   const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv,
                   int64_t n_heads, int64_t head_dim, void* stream);

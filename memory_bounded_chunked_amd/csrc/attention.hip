@@ -29,9 +29,6 @@
 namespace dit {
 
 constexpr int ATT_BN = 64;  // keys per tile
-#ifndef DIT_ATT_NW
-#define DIT_ATT_NW 8  // wavefronts per workgroup of the bf16 kernel
-#endif
 
 template <typename T, int DH, int NW>
 struct AttLayout {
@@ -195,11 +192,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-#ifdef DIT_ATT_RESCALE_ALWAYS
-    if (true) {
-#else
     if (__any(mx > m_run)) {  // wave-uniform: rescale only when some running max moved
-#endif
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale_log2);
       m_run = m_new;
@@ -295,29 +288,49 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
   }
 }
 
-// bf16 variant with a one-tile software pipeline: the score MFMAs of tile
-// t+1 are issued interleaved with the softmax of tile t (VALU and the
-// transcendental unit), so the matrix cores stay busy while exponentials are
-// taken. K runs one tile ahead of V in the LDS rings: iteration t reads K
-// tile t+1 and V tile t, and refills the K slot of tile t (consumed one
-// iteration earlier) with tile t+2 and the V slot of tile t-1 with tile t+1.
-// The row sum is accumulated from the bf16-rounded P that enters the PV
-// product (v_dot2_f32_bf16 against 1.0), two elements per instruction, and O
-// is rescaled only when a running max grows by more than 2^8.
-template <int DH, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_bf16_kernel(const uint16_t* __restrict__ q, int64_t ldq,
-                                                                 const uint16_t* __restrict__ k, int64_t ldk,
-                                                                 const uint16_t* __restrict__ vt, int64_t ldvt,
-                                                                 uint16_t* __restrict__ o, int64_t ldo,
-                                                                 int64_t n_q, int64_t n_kv, float qk_scale_log2) {
-  using L = AttLayout<uint16_t, DH, NW>;
+// bf16 variant (8 waves) with a two-group schedule. Waves w and w+4 share a
+// SIMD, so waves 0-3 and 4-7 form two groups with one wave per SIMD each;
+// group 1 runs one phase behind group 0. A key tile is four phases, each
+// closed by a workgroup barrier:
+//   M1: read the K fragments of tile t from LDS; store K tile t+1 into the
+//       other K slot; load K tile t+2 into the staging registers
+//   C1: S^T = K Q^T (2 x QS MFMAs)
+//   M2: read the V^T fragments of tile t; the softmax of tile t; store V^T
+//       tile t+1; load V^T tile t+2
+//   C2: O^T += V^T P^T (4 x OT MFMAs)
+// so on every SIMD one wave issues MFMAs while the other reads LDS and runs
+// the softmax. Tile t+1 is complete in LDS (both groups' stores) a barrier
+// before either group reads it, and a slot is overwritten only after both
+// groups finished reading the tile it held; both groups pass the same
+// number of barriers.
+//
+// Softmax: fp32, exp2 with log2(e)/sqrt(dh) folded into one multiply-add.
+// Tile 0 sets each query's running max exactly. Later tiles are
+// exponentiated against the max in use, and only a query whose tile sum
+// leaves [0, 2^16] moves to its new max (its O and row sum rescaled, the
+// tile's P formed again); otherwise P may reach 2^8 per element, which fp32
+// and bf16 hold without loss of relative precision. The decision uses only
+// the query's own scores, so O does not depend on which queries share a
+// wavefront. P is rounded to bf16 and the row sum is accumulated from the
+// rounded values (v_dot2_f32_bf16 against 1.0), the ones that enter the PV
+// product; O is divided by the row sum at the end.
+//
+// Loads carry no branch: key rows past n_kv re-read the last key row (their
+// scores are masked to -inf), V^T chunks past n_kv re-read the last valid
+// chunk (still inside the row: ldvt is a multiple of 8 and at least n_kv)
+// and are zeroed when stored, and the tiles after the last reload the last
+// tile into a slot no later phase reads. The compiler then waits for each
+// staged tile by exact count instead of for every outstanding load.
+template <int DH>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_bf16_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
+    const uint16_t* __restrict__ vt, int64_t ldvt, uint16_t* __restrict__ o, int64_t ldo, int64_t n_q,
+    int64_t n_kv, float qk_scale_log2) {
+  using L = AttLayout<uint16_t, DH, 8>;
   constexpr int EPC = L::EPC, KCH = L::KCH, VCH = L::VCH, KRP = L::KRP, VRP = L::VRP;
   constexpr int K_TILE = L::K_TILE, V_TILE = L::V_TILE, K_LD = L::K_LD, V_LD = L::V_LD;
   constexpr int QS = L::QS, OT = L::OT, NTHR = L::NTHR;
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
-  // Head-major order, contiguous per XCD: the query tiles of one head run on
-  // one XCD at the same time and share that head's K/V tiles through its L2,
-  // so each head's K/V crosses from HBM about once per launch.
   const int64_t q_tiles = ceil_div(n_q, L::BM);
   const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);  // gridDim.x = q_tiles * heads
   const int64_t head_idx = logical / q_tiles, q_tile = logical % q_tiles;
@@ -328,6 +341,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;
   const int64_t q0 = q_tile * L::BM + wave * 32;
   const int64_t col0 = head_idx * DH;
 
@@ -340,96 +354,80 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                         : u32x4{0u, 0u, 0u, 0u};
   }
 
+  const int64_t n_tiles = ceil_div(n_kv, ATT_BN);
+  const int64_t last_kv0 = (n_tiles - 1) * ATT_BN;
+  const bool ragged = (n_kv % ATT_BN) != 0;
   const char* kbase = reinterpret_cast<const char*>(k + col0);
   const char* vbase = reinterpret_cast<const char*>(vt + col0 * ldvt);
   const int64_t k_tile_bytes = (int64_t)ATT_BN * ldk * 2;
-  uint32_t koff[K_LD], voff[V_LD];
-  int kdst[K_LD], vdst[V_LD], krow[K_LD], vkey[V_LD];
-#pragma unroll
-  for (int i = 0; i < K_LD; ++i) {
-    const int c = tid + i * NTHR;
-    krow[i] = c / KCH;
-    koff[i] = (uint32_t)(((int64_t)krow[i] * ldk + (c % KCH) * EPC) * 2);
-    kdst[i] = krow[i] * KRP + (c % KCH) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < V_LD; ++i) {
-    const int c = tid + i * NTHR;
-    const int r = c / VCH, ch = c % VCH;
-    vkey[i] = ch * EPC;
-    voff[i] = (uint32_t)(((int64_t)r * ldvt + ch * EPC) * 2);
-    // keys 16j..16j+15 of a row: slot 2j holds keys {0-3, 8-11}, slot 2j+1
-    // holds {4-7, 12-15}, the order in which P^T sits in the S^T registers
-    vdst[i] = r * VRP + (ch >> 1) * 32 + 8 * (ch & 1);
-  }
+  // Per-thread chunks: thread tid moves chunk tid % KCH of K rows tid / KCH +
+  // i * (NTHR / KCH), and chunk tid % VCH of V^T rows tid / VCH + i * (NTHR /
+  // VCH), so every offset is one per-thread value plus a uniform step in i.
+  // In the last tile, K rows past n_kv are read from the last valid row and
+  // V^T chunks that start past n_kv from the last valid chunk.
+  constexpr int KRS = NTHR / KCH, VRS = NTHR / VCH;  // row steps between a thread's chunks
+  static_assert(NTHR % KCH == 0 && NTHR % VCH == 0, "chunk rows");
+  const int krow0 = tid / KCH, kch = tid % KCH;
+  const int vrow0 = tid / VCH, vch = tid % VCH, vkey = vch * EPC;
+  const uint32_t koff0 = (uint32_t)(((int64_t)krow0 * ldk + kch * EPC) * 2);
+  const int kv_last = (int)(n_kv - last_kv0);  // valid keys in the last tile, 1..64
+  const uint32_t kclamp = (uint32_t)(((int64_t)(kv_last - 1) * ldk + kch * EPC) * 2);
+  const uint32_t kstep = (uint32_t)((int64_t)KRS * ldk * 2);
+  const int64_t vkl = last_kv0 + vkey < n_kv ? vkey : ((n_kv - 1) & ~(int64_t)(EPC - 1)) - last_kv0;
+  const uint32_t voff0 = (uint32_t)(((int64_t)vrow0 * ldvt + vkey) * 2);
+  const uint32_t vclamp0 = (uint32_t)(((int64_t)vrow0 * ldvt + vkl) * 2);
+  const uint32_t vstep = (uint32_t)((int64_t)VRS * ldvt * 2);
+  const int kdst0 = krow0 * KRP + kch * 16;
+  // keys 16j..16j+15 of a V^T row: slot 2j holds keys {0-3, 8-11}, slot
+  // 2j+1 holds {4-7, 12-15}, the order in which P^T sits in the S^T registers
+  const int vdst0 = vrow0 * VRP + (vch >> 1) * 32 + 8 * (vch & 1);
 
   u32x4 rk[K_LD], rv[V_LD];
-  auto load_k = [&](int64_t t) {
+  auto load_k = [&](int64_t t) {  // t <= n_tiles - 1
     const char* src = kbase + t * k_tile_bytes;
-    const int64_t kv0 = t * ATT_BN;
-    if (kv0 + ATT_BN <= n_kv) {
+    const bool lt = t == n_tiles - 1;
 #pragma unroll
-      for (int i = 0; i < K_LD; ++i) rk[i] = *reinterpret_cast<const u32x4*>(src + koff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < K_LD; ++i)
-        rk[i] = (kv0 + krow[i] < n_kv) ? *reinterpret_cast<const u32x4*>(src + koff[i]) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < K_LD; ++i) {
+      const bool clamp = lt && krow0 + i * KRS >= kv_last;
+      rk[i] = *reinterpret_cast<const u32x4*>(src + (clamp ? kclamp : koff0 + i * kstep));
     }
   };
   auto load_v = [&](int64_t t) {
     const char* src = vbase + t * (int64_t)ATT_BN * 2;
-    const int64_t kv0 = t * ATT_BN;
-    if (kv0 + ATT_BN <= n_kv) {
+    const uint32_t base = t == n_tiles - 1 ? vclamp0 : voff0;
 #pragma unroll
-      for (int i = 0; i < V_LD; ++i) rv[i] = *reinterpret_cast<const u32x4*>(src + voff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < V_LD; ++i) {
-        const int64_t key = kv0 + vkey[i];
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(src + voff[i]);
-        uint16_t tmp[EPC];
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) tmp[j] = (key + j < n_kv) ? e[j] : (uint16_t)0;
-        rv[i] = __builtin_bit_cast(u32x4, tmp);
-      }
-    }
+    for (int i = 0; i < V_LD; ++i) rv[i] = *reinterpret_cast<const u32x4*>(src + base + i * vstep);
   };
   auto store_k = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) *reinterpret_cast<u32x4*>(kring + slot * K_TILE + kdst[i]) = rk[i];
+    for (int i = 0; i < K_LD; ++i)
+      *reinterpret_cast<u32x4*>(kring + slot * K_TILE + kdst0 + i * KRS * KRP) = rk[i];
   };
-  auto store_v = [&](int slot) {
-    char* vs = vring + slot * V_TILE;
+  auto store_v = [&](int slot, int64_t t) {  // t: the tile the staging registers hold
+    if (ragged && t == n_tiles - 1) {  // keys past n_kv read as zero
+      // (the empty asm keeps these compares here rather than hoisted out of
+      // the key loop, where their results would hold registers throughout)
+      int key = vkey;
+      asm volatile("" : "+v"(key));
+#pragma unroll
+      for (int i = 0; i < V_LD; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = key + 2 * w < kv_last ? 0x0000ffffu : 0u;
+          const uint32_t hi = key + 2 * w + 1 < kv_last ? 0xffff0000u : 0u;
+          rv[i][w] &= lo | hi;
+        }
+    }
+    char* vs = vring + slot * V_TILE + vdst0;
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
-      *reinterpret_cast<u32x2*>(vs + vdst[i]) = u32x2{rv[i][0], rv[i][1]};
-      *reinterpret_cast<u32x2*>(vs + vdst[i] + 16) = u32x2{rv[i][2], rv[i][3]};
+      *reinterpret_cast<u32x2*>(vs + i * VRS * VRP) = u32x2{rv[i][0], rv[i][1]};
+      *reinterpret_cast<u32x2*>(vs + i * VRS * VRP + 16) = u32x2{rv[i][2], rv[i][3]};
     }
   };
 
   const int k_rd = l32 * KRP + half * 16;
   const int v_rd = l32 * VRP + half * 16;
-
-  // S^T of one key tile: 2 x (32 keys x 32 queries), 2*QS MFMAs; the K
-  // fragments of k-step st+1 are read from LDS while those of st are used.
-  auto scores = [&](int slot, f32x16 (&s)[2]) {
-    const char* ks = kring + slot * K_TILE + k_rd;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-    u32x4 a[2][2];
-    a[0][0] = *reinterpret_cast<const u32x4*>(ks);
-    a[0][1] = *reinterpret_cast<const u32x4*>(ks + 32 * KRP);
-#pragma unroll
-    for (int st = 0; st < QS; ++st) {
-      if (st + 1 < QS) {
-        a[(st + 1) & 1][0] = *reinterpret_cast<const u32x4*>(ks + (st + 1) * 32);
-        a[(st + 1) & 1][1] = *reinterpret_cast<const u32x4*>(ks + 32 * KRP + (st + 1) * 32);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        s[mt] = mfma32_bf16(__builtin_bit_cast(bf16x8, a[st & 1][mt]), __builtin_bit_cast(bf16x8, qf[st]), s[mt]);
-    }
-  };
 
   f32x16 acc_o[OT];
 #pragma unroll
@@ -437,20 +435,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float m_run = -INFINITY, l_run = 0.f;
   const bf2 ones = __builtin_bit_cast(bf2, 0x3f803f80u);
 
-  // Softmax of one tile, in two parts. rescale(): the tile's row max; a
-  // query whose max grew by more than 8 (log2 units) past the max in use
-  // moves to its new max and rescales its O and row sum. Otherwise the stale
-  // max stays in use and P may reach 2^8, which fp32 and bf16 hold without
-  // loss of relative precision. The decision is taken per query, from that
-  // query's own scores only (other lanes of the wave merely share the branch,
-  // with a factor of exactly 1), so O does not depend on which queries share
-  // a wavefront, i.e. on how the queries were sliced. exp_tile(): P = exp2 of
-  // the scaled scores minus the max in use, packed to bf16, and the row sum
-  // accumulated from the packed values.
-  //
-  // The two lanes of a query (l and l^32) each hold half of its keys; one
-  // v_permlane32_swap gives both of them the combined value, in the same
-  // operand order.
   auto pair_max = [](float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -474,20 +458,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     return lsum;
   };
-  // After a tile's P is formed against the max in use: a query whose tile
-  // sum left [0, 2^16] (or is not finite) moves to its new max, rescales its
-  // O and row sum, and forms P again; every other query keeps its max and
-  // its P (factor exactly 1).
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int q = 2; q < 16; ++q) mx = fmaxf(mx, s[0][q]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[1][q]);
+    return pair_max(mx);
+  };
   auto settle = [&](f32x16 (&s)[2], u32x4 (&pb)[4], float ls) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
     const bool move = !(__uint_as_float(r[0]) + __uint_as_float(r[1]) <= 65536.0f);
     if (__any(move)) {
-      float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-      for (int q = 2; q < 16; ++q) mx = fmaxf(mx, s[0][q]);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[1][q]);
-      mx = pair_max(mx);
+      const float mx = tile_max(s);
       const float m_new = move ? fmaxf(m_run, mx) : m_run;
       const float alpha = move ? __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale_log2) : 1.0f;
       m_run = m_new;
@@ -500,97 +483,96 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     l_run += ls;
   };
-
-  auto pv = [&](int slot, const u32x4 (&pb)[4]) {
-    const char* vs = vring + slot * V_TILE + v_rd;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int t = 0; t < OT; ++t) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vs + t * 32 * VRP + j * 32);
-        acc_o[t] = mfma32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[j]), acc_o[t]);
-      }
-  };
-
-  const int64_t n_tiles = ceil_div(n_kv, ATT_BN);
-  // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
-  load_k(0);
-  store_k(0);
-  if (n_tiles > 1) {
-    load_k(1);
-    store_k(1);
-  }
-  load_v(0);
-  store_v(0);
-  __syncthreads();
-  // One pipeline step: scores of tile t+1 into s_nxt, interleaved with the
-  // softmax of tile t (in s_cur), then PV of tile t, then the LDS refills.
-  auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    const bool more_k = t + 2 < n_tiles;
-    if (more_k) load_k(t + 2);
-    load_v(t + 1);
-    u32x4 pb[4];
-    scores((int)((t + 1) & 1), s_nxt);
-    const float ls = exp_tile(s_cur, pb);
-#pragma unroll
-    for (int i = 0; i < QS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS fragment reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-    }
-    settle(s_cur, pb, ls);
-    pv((int)(t & 1), pb);
-    if (more_k) store_k((int)(t & 1));
-    store_v((int)((t + 1) & 1));
-    __syncthreads();
-  };
-  // Keys past n_kv in the last tile get -inf. Register r of block mt holds
-  // key mt*32 + 8*(r/4) + 4*half + r%4; the lane part is folded into the
-  // threshold so that the per-register part stays a literal.
+  // keys past n_kv in the last tile: -inf (register r of block mt holds key
+  // mt*32 + 8*(r/4) + 4*half + r%4)
   auto mask_last = [&](f32x16 (&s)[2]) {
-    const int thr = (int)(n_kv - (n_tiles - 1) * ATT_BN) - 4 * half;
+    int thr = kv_last - 4 * half;
+    asm volatile("" : "+v"(thr));  // compares stay here, not hoisted out of the key loop
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (mt * 32 + 8 * (r >> 2) + (r & 3) >= thr) s[mt][r] = -INFINITY;
   };
-  auto last = [&](f32x16 (&s_cur)[2]) {
-    if (n_kv % ATT_BN != 0 && n_tiles > 1) mask_last(s_cur);
-    u32x4 pb[4];
-    settle(s_cur, pb, exp_tile(s_cur, pb));
-    pv((int)((n_tiles - 1) & 1), pb);
+  auto phase_end = []() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x16 sa[2], sb[2];
-  scores(0, sa);
-  // tile 0 sets each query's running max exactly
-  if (n_tiles == 1 && n_kv % ATT_BN != 0) mask_last(sa);
+  // prologue: tile 0 in slot 0, tile 1 (or the last tile again) in the staging registers
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0, 0);
   {
-    float mx = fmaxf(sa[0][0], sa[0][1]);
+    const int64_t t1 = n_tiles > 1 ? 1 : 0;
+    load_k(t1);
+    load_v(t1);
+  }
+  __syncthreads();
+  if (grp == 1) phase_end();
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int cur = (int)(t & 1);
+    const int64_t t2 = t + 2 < n_tiles ? t + 2 : n_tiles - 1;
+    // M1
+    u32x4 kf[QS][2];
+    {
+      const char* ks = kring + cur * K_TILE + k_rd;
 #pragma unroll
-    for (int q = 2; q < 16; ++q) mx = fmaxf(mx, sa[0][q]);
+      for (int st = 0; st < QS; ++st) {
+        kf[st][0] = *reinterpret_cast<const u32x4*>(ks + st * 32);
+        kf[st][1] = *reinterpret_cast<const u32x4*>(ks + 32 * KRP + st * 32);
+      }
+    }
+    store_k(cur ^ 1);
+    load_k(t2);
+    phase_end();
+    // C1
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sa[1][q]);
-    m_run = pair_max(mx);
+    for (int st = 0; st < QS; ++st)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        s[mt] = mfma32_bf16(__builtin_bit_cast(bf16x8, kf[st][mt]), __builtin_bit_cast(bf16x8, qf[st]), s[mt]);
+    phase_end();
+    // M2
+    u32x4 vf[4][OT];
+    {
+      const char* vs = vring + cur * V_TILE + v_rd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int ot = 0; ot < OT; ++ot) vf[j][ot] = *reinterpret_cast<const u32x4*>(vs + ot * 32 * VRP + j * 32);
+    }
+    // the LDS traffic of this phase (fragment reads, tile store) is issued
+    // first and runs under the softmax
+    if (ragged && t == n_tiles - 1) mask_last(s);
+    if (t == 0) m_run = tile_max(s);  // tile 0 sets each query's running max exactly
+    u32x4 pb[4];
+    settle(s, pb, exp_tile(s, pb));
+    store_v(cur ^ 1, t + 1 < n_tiles ? t + 1 : n_tiles - 1);
+    load_v(t2);
+    phase_end();
+    // C2
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot)
+        acc_o[ot] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf[j][ot]), __builtin_bit_cast(bf16x8, pb[j]), acc_o[ot]);
+    phase_end();
   }
-  int64_t t = 0;
-  for (; t + 2 < n_tiles; t += 2) {  // only the last tile can be ragged
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
-  }
-  if (t + 1 < n_tiles) {
-    step(t, sa, sb);
-    last(sb);
-  } else {
-    last(sa);
-  }
+  if (grp == 0) phase_end();
 
   const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float inv = 1.0f / (__uint_as_float(lr[0]) + __uint_as_float(lr[1]));
-  const int64_t qr = q0 + l32;
+  // the output address is formed here from the thread id (passed through an
+  // empty asm), not kept in registers across the key loop
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int64_t qr = q_tile * L::BM + (tid_e >> 6) * 32 + (tid_e & 31);
   if (qr < n_q) {
     uint16_t* orow = o + qr * ldo + col0;
 #pragma unroll
@@ -605,14 +587,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int DH, int NW>
+template <int DH>
 static hipError_t launch_att_bf16(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
                                   int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int n_heads,
                                   hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
   // one-dimensional grid: the kernel derives (head, query tile) from blockIdx.x
-  dim3 grid((unsigned)(ceil_div(n_q, AttLayout<uint16_t, DH, NW>::BM) * n_heads)), block(NW * 64);
-  hipLaunchKernelGGL((attention_bf16_kernel<DH, NW>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
+  dim3 grid((unsigned)(ceil_div(n_q, AttLayout<uint16_t, DH, 8>::BM) * n_heads)), block(512);
+  hipLaunchKernelGGL((attention_bf16_kernel<DH>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
                      static_cast<const uint16_t*>(k), ldk, static_cast<const uint16_t*>(vt), ldvt,
                      static_cast<uint16_t*>(o), ldo, n_q, n_kv, scale_log2);
   return hipGetLastError();
@@ -641,8 +623,8 @@ hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k
     if (head_dim == 64) return launch_att_t<float, 64, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
     if (head_dim == 128) return launch_att_t<float, 128, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
   } else {
-    if (head_dim == 64) return launch_att_bf16<64, DIT_ATT_NW>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
-    if (head_dim == 128) return launch_att_bf16<128, DIT_ATT_NW>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 64) return launch_att_bf16<64>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 128) return launch_att_bf16<128>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
   }
   return hipErrorInvalidValue;
 }
