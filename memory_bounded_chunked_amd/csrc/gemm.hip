@@ -459,13 +459,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 
   // int8 weights: the adapter term joins after the contraction and the
   // per-row scale (which belongs to W a only) is applied before it.
-  const float* bscale = g.bscale;
+  bool scaled = B_I8;  // the per-row weight scale still has to be applied
   if constexpr (B_I8) {
     if (g.lora_t != nullptr) {
       lora_phase();
-      bscale = nullptr;
+      scaled = false;
     }
   }
+  // Weight scale of output column c. The load carries no branch (the scale
+  // array is always present with int8 weights): a value loaded under a
+  // branch makes the compiler wait for every outstanding memory operation,
+  // stores included, wherever the value is used.
+  auto col_scale = [&](int64_t c) -> float {
+    if constexpr (B_I8) {
+      const float v = g.bscale[c];
+      return scaled ? v : 1.f;
+    } else {
+      return 1.f;
+    }
+  };
 
   // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
   if constexpr (EPI == EPI_GATEUP) {
@@ -474,11 +486,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int p = 0; p < NTL / 2; ++p) {
         const int64_t f = tn * (BN / 2) + ((wn * NTL + 2 * p) >> 1) * 32 + (lane & 31);
-        float sg = 1.f, su = 1.f;
-        if (bscale) {
-          sg = bscale[f];
-          su = bscale[f + g.up_offset];
-        }
+        const float sg = col_scale(f), su = col_scale(f + g.up_offset);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
           const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-          const float sc = bscale ? bscale[col] : 1.f;
+          const float sc = col_scale(col);
           TA* orow = out + (col - col_base) * ldo;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -526,7 +534,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < NTL; ++j) {
             const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-            const float sc = bscale ? bscale[col] : 1.f;
+            const float sc = col_scale(col);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -555,30 +563,46 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
         }
       }
   } else {
+    // Per 32x32 block: the 16 operand values this lane needs (x for RESID,
+    // the fp32 stage for ACCUM and FINAL) are loaded together before any
+    // result is stored, so the block waits for memory once rather than once
+    // per element (the compiler may not move a load above a store that
+    // could alias it).
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NTL; ++j) {
         const int64_t col = tn * BN + wn * WTN + j * 32 + (lane & 31);
-        const float sc = bscale ? bscale[col] : 1.f;
+        const float sc = col_scale(col);
         const float gt = (EPI == EPI_STORE) ? 1.f : g.gate[col];
+        const int64_t row0 = m0 + wm * WTM + i * 32 + 4 * half;  // + 8 * (r / 4) + r % 4
+        float av[16];
+        if constexpr (EPI != EPI_STORE) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // rows past M read row M-1 (no branch around the load); their
+            // results are not stored
+            int64_t row = row0 + 8 * (r >> 2) + (r & 3);
+            row = row < g.M ? row : g.M - 1;
+            if constexpr (EPI == EPI_RESID)
+              av[r] = load_act(static_cast<const TA*>(g.aux) + row * g.ldaux + col);
+            else if constexpr (EPI == EPI_ACCUM)
+              av[r] = static_cast<const float*>(g.out)[row * g.ldo + col];
+            else  // EPI_FINAL
+              av[r] = static_cast<const float*>(g.aux)[row * g.ldaux + col];
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int64_t row = row0 + 8 * (r >> 2) + (r & 3);
           if (row >= g.M) continue;
           const float v = acc[i][j][r] * sc;
-          if constexpr (EPI == EPI_STORE) {
+          if constexpr (EPI == EPI_STORE)
             store_act(static_cast<TA*>(g.out) + row * g.ldo + col, v);
-          } else if constexpr (EPI == EPI_RESID) {
-            const float xv = load_act(static_cast<const TA*>(g.aux) + row * g.ldaux + col);
-            static_cast<float*>(g.out)[row * g.ldo + col] = xv + gt * v;
-          } else if constexpr (EPI == EPI_ACCUM) {
-            float* o = static_cast<float*>(g.out) + row * g.ldo + col;
-            *o = *o + gt * v;
-          } else {  // EPI_FINAL
-            const float sv = static_cast<const float*>(g.aux)[row * g.ldaux + col];
-            store_act(static_cast<TA*>(g.out) + row * g.ldo + col, sv + gt * v);
-          }
+          else if constexpr (EPI == EPI_RESID || EPI == EPI_ACCUM)
+            static_cast<float*>(g.out)[row * g.ldo + col] = av[r] + gt * v;
+          else  // EPI_FINAL
+            store_act(static_cast<TA*>(g.out) + row * g.ldo + col, av[r] + gt * v);
         }
       }
   }
