@@ -128,12 +128,19 @@ __global__ __launch_bounds__(LoraT<NT>::NTHR) void lora_t_kernel(const uint16_t*
     }
     const int64_t n = nt * 32 + l32;
     if (n >= rank) continue;
+    // the 16 previous values are read together, before any store, from
+    // clamped rows (no load under a branch), and used only when accumulating
+    float prev[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t mr = m0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      prev[r] = t[(mr < m ? mr : m - 1) * ldt + n];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t mr = m0 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (mr >= m) continue;
-      float* o = t + mr * ldt + n;
-      *o = (accumulate ? *o : 0.f) + alpha * sum[r];
+      t[mr * ldt + n] = (accumulate ? prev[r] : 0.f) + alpha * sum[r];
     }
   }
 }

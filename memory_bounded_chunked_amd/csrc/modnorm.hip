@@ -24,43 +24,48 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const Tin* __restrict__ x,
   if (row >= rows) return;
   const int ngroups = d >> 3;
   const Tin* xr = x + row * ldx;
+  // Lanes whose group index passes the row end load the last group again
+  // and leave it out of the sums and the stores: no load sits under a
+  // branch, so all of them are in flight together (a load under a branch
+  // makes the compiler wait for it, and for every store before it, at once).
   float v[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = g * 64 + lane < ngroups ? g * 64 + lane : ngroups - 1;
+    if constexpr (sizeof(Tin) == 2) {
+      const u32x4 p = *reinterpret_cast<const u32x4*>(xr + idx * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[g][2 * j] = __uint_as_float(p[j] << 16);
+        v[g][2 * j + 1] = __uint_as_float(p[j] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(xr + idx * 8);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(xr + idx * 8 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[g][j] = p0[j];
+        v[g][4 + j] = p1[j];
+      }
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int idx = g * 64 + lane;
-    if (idx < ngroups) {
-      if constexpr (sizeof(Tin) == 2) {
-        const u32x4 p = *reinterpret_cast<const u32x4*>(xr + idx * 8);
+    const bool ok = g * 64 + lane < ngroups;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[g][2 * j] = __uint_as_float(p[j] << 16);
-          v[g][2 * j + 1] = __uint_as_float(p[j] & 0xffff0000u);
-        }
-      } else {
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(xr + idx * 8);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(xr + idx * 8 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[g][j] = p0[j];
-          v[g][4 + j] = p1[j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += v[g][j];
-    }
+    for (int j = 0; j < 8; ++j) s += ok ? v[g][j] : 0.f;
   }
   const float inv_d = 1.0f / (float)d;
   const float mu = wave_sum(s) * inv_d;
   float s2 = 0.f;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (g * 64 + lane < ngroups) {
+    const bool ok = g * 64 + lane < ngroups;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float t = v[g][j] - mu;
-        s2 += t * t;
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float t = v[g][j] - mu;
+      s2 = ok ? __builtin_fmaf(t, t, s2) : s2;
     }
   }
   const float var = wave_sum(s2) * inv_d;
@@ -68,27 +73,27 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const Tin* __restrict__ x,
   Tout* orow = out + row * ldo;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int idx = g * 64 + lane;
-    if (idx < ngroups) {
-      const f32x4 sc0 = *reinterpret_cast<const f32x4*>(scale + idx * 8);
-      const f32x4 sc1 = *reinterpret_cast<const f32x4*>(scale + idx * 8 + 4);
-      const f32x4 sh0 = *reinterpret_cast<const f32x4*>(shift + idx * 8);
-      const f32x4 sh1 = *reinterpret_cast<const f32x4*>(shift + idx * 8 + 4);
-      float o[8];
+    const bool ok = g * 64 + lane < ngroups;
+    const int idx = ok ? g * 64 + lane : ngroups - 1;
+    const f32x4 sc0 = *reinterpret_cast<const f32x4*>(scale + idx * 8);
+    const f32x4 sc1 = *reinterpret_cast<const f32x4*>(scale + idx * 8 + 4);
+    const f32x4 sh0 = *reinterpret_cast<const f32x4*>(shift + idx * 8);
+    const f32x4 sh1 = *reinterpret_cast<const f32x4*>(shift + idx * 8 + 4);
+    float o[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j] = (v[g][j] - mu) * rstd * (1.0f + sc0[j]) + sh0[j];
-        o[4 + j] = (v[g][4 + j] - mu) * rstd * (1.0f + sc1[j]) + sh1[j];
-      }
-      if constexpr (sizeof(Tout) == 2) {
-        u32x4 p;
+    for (int j = 0; j < 4; ++j) {  // n = ((x - mu) * rstd) * (1 + scale) + shift, the last step fused
+      o[j] = __builtin_fmaf((v[g][j] - mu) * rstd, 1.0f + sc0[j], sh0[j]);
+      o[4 + j] = __builtin_fmaf((v[g][4 + j] - mu) * rstd, 1.0f + sc1[j], sh1[j]);
+    }
+    if (!ok) continue;
+    if constexpr (sizeof(Tout) == 2) {
+      u32x4 p;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
-        *reinterpret_cast<u32x4*>(orow + idx * 8) = p;
-      } else {
-        *reinterpret_cast<f32x4*>(orow + idx * 8) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(orow + idx * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      }
+      for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(orow + idx * 8) = p;
+    } else {
+      *reinterpret_cast<f32x4*>(orow + idx * 8) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(orow + idx * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
     }
   }
 }

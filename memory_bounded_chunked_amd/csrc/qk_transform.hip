@@ -29,66 +29,74 @@ __global__ __launch_bounds__(256) void qk_transform_kernel(T* __restrict__ x, in
   const int ngroups = d >> 3;
   const int hg = lane % LPH;  // this lane's 8-element group within its head
   T* xr = x + row * ldx;
+  // Every load is issued before any store and none sits under a per-lane
+  // branch: lanes past the row end re-read the last group (whole heads are
+  // valid or invalid together, so the per-head sums never mix the two) and
+  // store nothing. The norm weights and the angles depend only on the lane's
+  // place in its head, so they are read once.
+  float v[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = g * 64 + lane < ngroups ? g * 64 + lane : ngroups - 1;
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 p = *reinterpret_cast<const u32x4*>(xr + idx * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[g][2 * j] = __uint_as_float(p[j] << 16);
+        v[g][2 * j + 1] = __uint_as_float(p[j] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(xr + idx * 8);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(xr + idx * 8 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[g][j] = p0[j];
+        v[g][4 + j] = p1[j];
+      }
+    }
+  }
+  f32x4 w0 = f32x4{1.f, 1.f, 1.f, 1.f}, w1 = w0, c = w0, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (w) {
+    w0 = *reinterpret_cast<const f32x4*>(w + hg * 8);
+    w1 = *reinterpret_cast<const f32x4*>(w + hg * 8 + 4);
+  }
+  if (cs) {
+    c = *reinterpret_cast<const f32x4*>(cs + row * ld_rope + hg * 4);
+    sv = *reinterpret_cast<const f32x4*>(sn + row * ld_rope + hg * 4);
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int idx = g * 64 + lane;
-    const bool valid = idx < ngroups;  // whole heads are valid or invalid together
-    float v[8];
-    if (valid) {
-      if constexpr (sizeof(T) == 2) {
-        const u32x4 p = *reinterpret_cast<const u32x4*>(xr + idx * 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = __uint_as_float(p[j] << 16);
-          v[2 * j + 1] = __uint_as_float(p[j] & 0xffff0000u);
-        }
-      } else {
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(xr + idx * 8);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(xr + idx * 8 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] = p0[j];
-          v[4 + j] = p1[j];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
-    }
     if (w) {
       float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+      for (int j = 0; j < 8; ++j) ss += v[g][j] * v[g][j];
 #pragma unroll
       for (int off = 1; off < LPH; off <<= 1) ss += __shfl_xor(ss, off, 64);
       const float r = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + hg * 8);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + hg * 8 + 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[j] = v[j] * r * w0[j];
-        v[4 + j] = v[4 + j] * r * w1[j];
+        v[g][j] = v[g][j] * r * w0[j];
+        v[g][4 + j] = v[g][4 + j] * r * w1[j];
       }
     }
-    if (!valid) continue;
+    if (idx >= ngroups) continue;
     if (cs) {
-      const f32x4 c = *reinterpret_cast<const f32x4*>(cs + row * ld_rope + hg * 4);
-      const f32x4 s = *reinterpret_cast<const f32x4*>(sn + row * ld_rope + hg * 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = v[2 * j], b = v[2 * j + 1];
-        v[2 * j] = a * c[j] - b * s[j];
-        v[2 * j + 1] = a * s[j] + b * c[j];
+        const float a = v[g][2 * j], b = v[g][2 * j + 1];
+        v[g][2 * j] = a * c[j] - b * sv[j];
+        v[g][2 * j + 1] = a * sv[j] + b * c[j];
       }
     }
     if constexpr (sizeof(T) == 2) {
       u32x4 p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(v[g][2 * j], v[g][2 * j + 1]);
       *reinterpret_cast<u32x4*>(xr + idx * 8) = p;
     } else {
-      *reinterpret_cast<f32x4*>(xr + idx * 8) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(xr + idx * 8 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      *reinterpret_cast<f32x4*>(xr + idx * 8) = f32x4{v[g][0], v[g][1], v[g][2], v[g][3]};
+      *reinterpret_cast<f32x4*>(xr + idx * 8 + 4) = f32x4{v[g][4], v[g][5], v[g][6], v[g][7]};
     }
   }
 }
