@@ -24,7 +24,9 @@ def _rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 
 
-@pytest.mark.parametrize("rows,d", [(1, 256), (37, 256), (1000, 3072), (515, 5120)])
+# d = 8 and 520: a single 8-element group, and one group past a multiple of
+# 64 lanes (the lanes past the row end re-read the last group and store nothing)
+@pytest.mark.parametrize("rows,d", [(1, 256), (37, 256), (1000, 3072), (515, 5120), (5, 8), (33, 520)])
 def test_modnorm_bf16(rows, d):
     rng = _rng(rows + d)
     x = synth.bf16_bits_to_f64(synth.f64_to_bf16_bits(rng.standard_normal((rows, d)) * 1.7 + 0.3))
