@@ -6,9 +6,9 @@
 // buffered: the next k-tile's global loads are in flight while the current
 // one is multiplied); WM x WN wavefronts (8 for BN = 256 or 128: two per
 // SIMD) each compute a (256/WM) x (BN/WN) block with accumulators in VGPRs.
-// With 8 waves and bf16 activations the two waves of each SIMD run one
-// phase apart (the two-group schedule at the main loop), so one multiplies
-// while the other reads LDS.
+// With 8 waves and bf16 weights the two waves of each SIMD run one phase
+// apart (the two-group schedule at the main loop), so one multiplies while
+// the other reads LDS.
 // LDS rows hold 128 B of k and are padded to 144 B:
 // consecutive rows start 4 banks apart, so fragment reads are conflict-free
 // and their addresses are a per-lane base plus compile-time offsets.
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   store_tiles(0);
   if (KT > 1) load_tiles(BK);
   __syncthreads();
-  // Two-group schedule for 8 waves (bf16 activations). Waves 0-3 and 4-7 each
+  // Two-group schedule for 8 waves (bf16 weights). Waves 0-3 and 4-7 each
   // hold one wave per SIMD, and group 1 runs one phase behind group 0, so on
   // every SIMD one wave issues MFMAs while the other reads its next
   // fragments from LDS and moves the next tile in. A k-tile is four phases,
@@ -410,7 +410,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // both groups (group 1 takes one more before the loop, group 0 one more
   // after it). Each accumulator still takes k-steps 0, 1, 2, 3 of each tile in
   // order, as in the one-group schedule.
-  constexpr bool PP = !A_F32 && WM * WN == 8;
+  // (int8 weights keep the one-group schedule: their widening to bf16 on the
+  // way into LDS made the two-group one 3-8% slower)
+  constexpr bool PP = !A_F32 && !B_I8 && WM * WN == 8;
   int kt = 0;
   if constexpr (PP) {
     const int grp = wave >> 2;
