@@ -310,8 +310,114 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
             }
           }
         };
-        sweep(std::integral_constant<int, 0>{});
-        if constexpr (!A_F32) sweep(std::integral_constant<int, 1>{});
+        if constexpr (A_F32) {
+          sweep(std::integral_constant<int, 0>{});
+        } else if constexpr (B_I8) {
+          // int8 weights: this phase follows the main loop with every
+          // accumulator live, so its fragments come straight from global
+          // memory (staging them through LDS needs registers the loop state
+          // already holds)
+          sweep(std::integral_constant<int, 0>{});
+          sweep(std::integral_constant<int, 1>{});
+        } else {
+          // bf16: t and the adapter's B rows for this tile are staged through
+          // LDS in rank chunks of 64 (all global loads of a chunk in flight
+          // at once), then the two sweeps read their fragments from LDS. The
+          // accumulation order is that of the two sweeps above.
+          constexpr int RC = 64;                      // rank chunk
+          constexpr int TROW = RC * 4 + 16;           // LDS row of t (fp32), padded
+          constexpr int BROW = RC * 2 + 16;           // LDS row of B (bf16), padded
+          constexpr int T_CH = BM * (RC / 4), B_CH = BN * (RC / 8);  // 16-B chunks
+          static_assert(BM * TROW + BN * BROW <= 2 * STAGE, "adapter staging fits the tile buffers");
+          static_assert(T_CH % NTHR == 0 && B_CH % NTHR == 0, "adapter staging chunks");
+          char* const ts = smem;
+          char* const bs = smem + BM * TROW;
+          auto stage = [&](int64_t c0) {
+            const int64_t kc = r - c0 < RC ? r - c0 : RC;
+            u32x4 rt[T_CH / NTHR], rbv[B_CH / NTHR];
+#pragma unroll
+            for (int q = 0; q < T_CH / NTHR; ++q) {
+              const int c = tid + q * NTHR, row = c / (RC / 4), ch = c % (RC / 4);
+              const int64_t gr = m0 + row < g.M ? m0 + row : g.M - 1;
+              const int64_t col = ch * 4 < kc ? g.lora_toff[SG] + c0 + ch * 4 : g.lora_toff[SG] + c0;
+              rt[q] = *reinterpret_cast<const u32x4*>(g.lora_t + gr * g.lora_ldt + col);
+            }
+#pragma unroll
+            for (int q = 0; q < B_CH / NTHR; ++q) {
+              const int c = tid + q * NTHR, cb = c / (RC / 8), ch = c % (RC / 8);
+              int64_t brw;  // adapter row of tile column cb (any valid row for other segments)
+              if constexpr (EPI == EPI_GATEUP) {
+                brw = tn * (BN / 2) + ((cb >> 5) >> 1) * 32 + (cb & 31);
+              } else {
+                const int64_t colg = tn * BN + cb;
+                brw = (EPI == EPI_KV && colg >= g.split) ? colg - g.split : colg;
+              }
+              const int64_t kk = ch * 8 < kc ? c0 + ch * 8 : c0;
+              rbv[q] = *reinterpret_cast<const u32x4*>(bbase + brw * r + kk);
+            }
+            __syncthreads();  // every wave is done with the previous contents
+#pragma unroll
+            for (int q = 0; q < T_CH / NTHR; ++q) {
+              const int c = tid + q * NTHR;
+              *reinterpret_cast<u32x4*>(ts + (c / (RC / 4)) * TROW + (c % (RC / 4)) * 16) = rt[q];
+            }
+#pragma unroll
+            for (int q = 0; q < B_CH / NTHR; ++q) {
+              const int c = tid + q * NTHR;
+              *reinterpret_cast<u32x4*>(bs + (c / (RC / 8)) * BROW + (c % (RC / 8)) * 16) = rbv[q];
+            }
+            __syncthreads();
+          };
+          auto sweep_lds = [&](auto part_c, int64_t c0) {
+            constexpr int PART = decltype(part_c)::value;
+            const int64_t kc = r - c0 < RC ? r - c0 : RC;
+            for (int64_t k0 = 0; k0 < kc; k0 += 16) {
+              u32x4 bfr[NTL];
+#pragma unroll
+              for (int j = 0; j < NTL; ++j) {
+                if (EPI == EPI_GATEUP && (j & 1) != SG) continue;
+                bfr[j] = *reinterpret_cast<const u32x4*>(bs + (wn * WTN + j * 32 + l32) * BROW + (k0 + 8 * hf) * 2);
+              }
+#pragma unroll
+              for (int i = 0; i < MT; ++i) {
+                const char* tp = ts + (wm * WTM + i * 32 + l32) * TROW + (k0 + 8 * hf) * 4;
+                const f32x4 t0 = *reinterpret_cast<const f32x4*>(tp);
+                const f32x4 t1 = *reinterpret_cast<const f32x4*>(tp + 16);
+                const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+                uint32_t wv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  wv[q] = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
+                  if constexpr (PART == 1)
+                    wv[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wv[q] << 16),
+                                        tv[2 * q + 1] - __uint_as_float(wv[q] & 0xffff0000u));
+                }
+                const u32x4 af = u32x4{wv[0], wv[1], wv[2], wv[3]};
+#pragma unroll
+                for (int j = 0; j < NTL; ++j)
+                  if (EPI != EPI_GATEUP || (j & 1) == SG)
+                    acc[i][j] = mfma32_bf16(__builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfr[j]),
+                                            acc[i][j]);
+              }
+            }
+          };
+          if (r <= RC) {
+            if (r > 0) {
+              stage(0);
+              sweep_lds(std::integral_constant<int, 0>{}, 0);
+              sweep_lds(std::integral_constant<int, 1>{}, 0);
+            }
+          } else {
+            for (int64_t c0 = 0; c0 < r; c0 += RC) {
+              stage(c0);
+              sweep_lds(std::integral_constant<int, 0>{}, c0);
+            }
+            for (int64_t c0 = 0; c0 < r; c0 += RC) {
+              stage(c0);
+              sweep_lds(std::integral_constant<int, 1>{}, c0);
+            }
+          }
+        }
       };
       if constexpr (EPI == EPI_GATEUP) {
         lora_seg(std::integral_constant<int, 0>{});
@@ -388,7 +494,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // tile kt+2. One barrier per k-tile.
   const int KT = (int)(g.K / BK);
   if constexpr (!B_I8) {
-    if (g.lora_t != nullptr) lora_phase();
+    if (g.lora_t != nullptr) {
+      lora_phase();
+      __syncthreads();  // the adapter staging area is the tile buffers
+    }
   }
   load_tiles(0);
   store_tiles(0);

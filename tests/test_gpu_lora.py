@@ -160,6 +160,23 @@ def test_single_adapter_on_each_projection(shape, bar):
         assert rel_l2(y - y0, y_ref - y0_ref) <= bar, name
 
 
+@pytest.mark.parametrize("rank", [80, 256])
+def test_lora_rank_above_one_staging_chunk(rank):
+    # bf16 adapters are staged through LDS in rank chunks of 64; ranks of 80
+    # (a ragged second chunk) and 256 (four chunks), on every projection
+    shape = SMALL["bf16"]
+    inputs = synth.make_inputs(shape, seed=0)
+    lora = synth.make_lora(shape, rank, seed=3)
+    x, mod, w = oracle_inputs(inputs)
+    y_ref = O.block_forward(x, mod, w, shape.n_heads, lora=_lora_f64(lora))
+    y0_ref = O.block_forward(x, mod, w, shape.n_heads)
+    y = to_f64(_run(shape, inputs, lora, 256, 256))
+    y0 = to_f64(_run(shape, inputs, None, 256, 256))
+    check_bf16_bar(y, y_ref)
+    assert rel_l2(y - y0, y_ref - y0_ref) <= 3e-2
+    assert bits(_run(shape, inputs, lora, 100, 300)) == bits(_run(shape, inputs, lora, 256, 256))
+
+
 @pytest.mark.timeout(900)
 def test_lora_mid_block_sampled_rows():
     # the 16k-token, d=3072 block with rank-64 adapters on every projection,
