@@ -88,7 +88,11 @@ __device__ __forceinline__ void store_act(T* p, float v) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
-template <typename TA, typename TB, int EPI, int BM, int BN, int WM, int WN>
+// LO: whether the kernel carries the adapter phase. int8-weight kernels come
+// in both forms, because that phase follows their main loop and its
+// registers would otherwise cost every int8 launch (spills after the loop);
+// the others always carry it (it runs before the loop, or in fp32).
+template <typename TA, typename TB, int EPI, int BM, int BN, int WM, int WN, bool LO>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   constexpr int NTHR = WM * WN * 64;
   constexpr bool A_F32 = sizeof(TA) == 4;
@@ -312,13 +316,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
         };
         if constexpr (A_F32) {
           sweep(std::integral_constant<int, 0>{});
-        } else if constexpr (B_I8) {
-          // int8 weights: this phase follows the main loop with every
-          // accumulator live, so its fragments come straight from global
-          // memory (staging them through LDS needs registers the loop state
-          // already holds)
-          sweep(std::integral_constant<int, 0>{});
-          sweep(std::integral_constant<int, 1>{});
         } else {
           // bf16: t and the adapter's B rows for this tile are staged through
           // LDS in rank chunks of 64 (all global loads of a chunk in flight
@@ -332,19 +329,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
           static_assert(T_CH % NTHR == 0 && B_CH % NTHR == 0, "adapter staging chunks");
           char* const ts = smem;
           char* const bs = smem + BM * TROW;
+          // Chunk job j < NTJ moves a 16-B piece of t, job NTJ + q a 16-B piece
+          // of B. With int8 weights (this phase then follows the main loop,
+          // every accumulator live) the jobs run in batches of 4 to keep the
+          // staging registers few; otherwise all loads are in flight at once.
+          constexpr int NTJ = T_CH / NTHR, NBJ = B_CH / NTHR, NJ = NTJ + NBJ;
+          constexpr int BATCH = B_I8 ? 4 : NJ;
           auto stage = [&](int64_t c0) {
             const int64_t kc = r - c0 < RC ? r - c0 : RC;
-            u32x4 rt[T_CH / NTHR], rbv[B_CH / NTHR];
-#pragma unroll
-            for (int q = 0; q < T_CH / NTHR; ++q) {
-              const int c = tid + q * NTHR, row = c / (RC / 4), ch = c % (RC / 4);
-              const int64_t gr = m0 + row < g.M ? m0 + row : g.M - 1;
-              const int64_t col = ch * 4 < kc ? g.lora_toff[SG] + c0 + ch * 4 : g.lora_toff[SG] + c0;
-              rt[q] = *reinterpret_cast<const u32x4*>(g.lora_t + gr * g.lora_ldt + col);
-            }
-#pragma unroll
-            for (int q = 0; q < B_CH / NTHR; ++q) {
-              const int c = tid + q * NTHR, cb = c / (RC / 8), ch = c % (RC / 8);
+            auto load_job = [&](int j) -> u32x4 {
+              if (j < NTJ) {
+                const int c = tid + j * NTHR, row = c / (RC / 4), ch = c % (RC / 4);
+                const int64_t gr = m0 + row < g.M ? m0 + row : g.M - 1;
+                const int64_t col = ch * 4 < kc ? g.lora_toff[SG] + c0 + ch * 4 : g.lora_toff[SG] + c0;
+                return *reinterpret_cast<const u32x4*>(g.lora_t + gr * g.lora_ldt + col);
+              }
+              const int c = tid + (j - NTJ) * NTHR, cb = c / (RC / 8), ch = c % (RC / 8);
               int64_t brw;  // adapter row of tile column cb (any valid row for other segments)
               if constexpr (EPI == EPI_GATEUP) {
                 brw = tn * (BN / 2) + ((cb >> 5) >> 1) * 32 + (cb & 31);
@@ -353,18 +353,27 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
                 brw = (EPI == EPI_KV && colg >= g.split) ? colg - g.split : colg;
               }
               const int64_t kk = ch * 8 < kc ? c0 + ch * 8 : c0;
-              rbv[q] = *reinterpret_cast<const u32x4*>(bbase + brw * r + kk);
-            }
-            __syncthreads();  // every wave is done with the previous contents
+              return *reinterpret_cast<const u32x4*>(bbase + brw * r + kk);
+            };
+            auto store_job = [&](int j, const u32x4& v) {
+              if (j < NTJ) {
+                const int c = tid + j * NTHR;
+                *reinterpret_cast<u32x4*>(ts + (c / (RC / 4)) * TROW + (c % (RC / 4)) * 16) = v;
+              } else {
+                const int c = tid + (j - NTJ) * NTHR;
+                *reinterpret_cast<u32x4*>(bs + (c / (RC / 8)) * BROW + (c % (RC / 8)) * 16) = v;
+              }
+            };
 #pragma unroll
-            for (int q = 0; q < T_CH / NTHR; ++q) {
-              const int c = tid + q * NTHR;
-              *reinterpret_cast<u32x4*>(ts + (c / (RC / 4)) * TROW + (c % (RC / 4)) * 16) = rt[q];
-            }
+            for (int j0 = 0; j0 < NJ; j0 += BATCH) {
+              u32x4 rr[BATCH];
 #pragma unroll
-            for (int q = 0; q < B_CH / NTHR; ++q) {
-              const int c = tid + q * NTHR;
-              *reinterpret_cast<u32x4*>(bs + (c / (RC / 8)) * BROW + (c % (RC / 8)) * 16) = rbv[q];
+              for (int q = 0; q < BATCH; ++q)
+                if (j0 + q < NJ) rr[q] = load_job(j0 + q);
+              if (j0 == 0) __syncthreads();  // every wave is done with the previous contents
+#pragma unroll
+              for (int q = 0; q < BATCH; ++q)
+                if (j0 + q < NJ) store_job(j0 + q, rr[q]);
             }
             __syncthreads();
           };
@@ -571,7 +580,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // int8 weights: the adapter term joins after the contraction and the
   // per-row scale (which belongs to W a only) is applied before it.
   bool scaled = B_I8;  // the per-row weight scale still has to be applied
-  if constexpr (B_I8) {
+  if constexpr (B_I8 && LO) {
     if (g.lora_t != nullptr) {
       lora_phase();
       scaled = false;
@@ -724,8 +733,15 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 256;
   constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   const int64_t tiles = ceil_div(g.M, BM) * ((g.N - g.col0) / OUT_BN);
-  hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0, st,
-                     g);
+  if constexpr (sizeof(TB) == 1) {
+    if (g.lora_t == nullptr) {
+      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, false>), dim3((unsigned)tiles),
+                         dim3(WM * WN * 64), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, true>), dim3((unsigned)tiles), dim3(WM * WN * 64),
+                     0, st, g);
   return hipGetLastError();
 }
 
