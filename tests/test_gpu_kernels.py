@@ -86,7 +86,10 @@ def _out_tol(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
-@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (300, 384, 512), (129, 256, 256)])
+# (257, 256, 64), (70, 512, 128), (33, 768, 192): one, two and three k-tiles in
+# the 8-wave tiles, whose schedule reloads the last k-tile at the end
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (300, 384, 512), (129, 256, 256), (257, 256, 64), (70, 512, 128),
+                                   (33, 768, 192)])
 def test_linear_store(dtype, m, n, k):
     a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, m + n + k)
     out = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
