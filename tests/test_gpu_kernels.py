@@ -100,6 +100,23 @@ def test_linear_store(dtype, m, n, k):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+def test_linear_tile_shape_does_not_change_bits(dtype):
+    # The same output columns through launches that pick different tiles (256
+    # or 128 or 64 weight rows per tile; 8 waves in two groups, or 4 waves):
+    # every element takes the same k sequence, so the bits must agree. The
+    # block's bit-identity across chunk sizes relies on this.
+    m, n, k = 300, 2048, 512
+    a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 21)
+    full = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "store", ta, tw, full, n, w_scale=ts)
+    for c0, width in ((0, 64), (64, 128), (256, 256), (512, 1536), (1984, 64)):
+        part = torch.empty(m, width, dtype=_act_dtype(dtype), device=DEV)
+        B.linear(dtype, "store", ta, tw[c0:c0 + width], part, width, w_scale=None if ts is None else ts[c0:c0 + width])
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu(), full[:, c0:c0 + width].cpu()), (c0, width)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
 def test_linear_store_transposed(dtype):
     m, n, k, ld = 203, 128, 256, 256
     a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 11)
