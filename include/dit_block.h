@@ -45,6 +45,8 @@ extern "C" {
 #define DIT_EINVAL (-1)  /* bad argument: null pointer, shape, chunk value, alignment */
 #define DIT_ENOSPC (-2)  /* workspace_bytes below dit_block_peak_workspace() */
 #define DIT_EHIP (-3)    /* the HIP runtime reported a launch error */
+#define DIT_ETOOBIG (-4) /* dit_block_forward_noalloc: the sizes need more than
+                            DIT_STATIC_WORKSPACE_BYTES of workspace */
 
 /* Storage types. F32: activations and weights fp32, fp32 arithmetic.
  * BF16: activations and weights bf16, fp32 accumulation and softmax.
@@ -172,6 +174,33 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
                            const float* rope_sin, int64_t n_tokens, int64_t attn_chunk_tokens,
                            int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as dit_block_forward_rope, with the workspace taken from a buffer
+ * the library owns instead of a caller argument.
+ *   The buffer is a static device array of DIT_STATIC_WORKSPACE_BYTES (64 MiB)
+ *   per GPU, loaded with the library's code and held until the process ends.
+ *   The first call on a device looks up that device's copy of the array
+ *   (hipGetSymbolAddress, host side, with that device current); no call
+ *   allocates device memory or calls hipMalloc / hipFree.
+ *   The current device's copy is used: `stream` must belong to the current
+ *   device.
+ *   Sizes whose dit_block_peak_workspace() exceeds DIT_STATIC_WORKSPACE_BYTES
+ *   are refused with DIT_ETOOBIG before anything is enqueued (for example a
+ *   bf16 block with d = 1024 and F = 4096 needs 44 MiB for 4096 tokens at
+ *   chunks of 2048, and 72 MiB at chunks of 4096, which is refused).
+ *   Every call on one GPU shares that GPU's buffer, and the buffer keeps the
+ *   last call's contents: the forward needs no part of it cleared (every
+ *   region is written before it is read), but calls that overlap in time on
+ *   one GPU (different streams, or different host threads) race on it and
+ *   must be serialised by the caller.
+ * Arguments, results and other errors as dit_block_forward_rope (rope tables
+ * may be NULL together). */
+#define DIT_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int dit_block_forward_noalloc(dit_block* h, void* x, const float* mod, const float* rope_cos,
+                              const float* rope_sin, int64_t n_tokens, int64_t attn_chunk_tokens,
+                              int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* stream);
 
 /* One activation-space adapter ("ComfyUI-StaticPipeline", section
  * "Activation-space LoRA (bypass mode)"): a projection y = W a of the block

@@ -16,7 +16,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit_block.so")
 _lib = None
 
-DIT_OK, DIT_EINVAL, DIT_ENOSPC, DIT_EHIP = 0, -1, -2, -3
+DIT_OK, DIT_EINVAL, DIT_ENOSPC, DIT_EHIP, DIT_ETOOBIG = 0, -1, -2, -3, -4
+# bytes of the library-owned workspace of dit_block_forward_noalloc (per GPU)
+STATIC_WORKSPACE_BYTES = 64 << 20
 DTYPES = {"f32": 0, "bf16": 1, "w8_bf16": 2}
 EPILOGUES = {"store": 0, "store_t": 1, "resid": 2, "gateup": 3, "accum": 4, "final": 5}
 
@@ -28,7 +30,7 @@ DEFAULT_MLP_CHUNK = 8192
 EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
            "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
            "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer",
-           "dit_block_set_lora")
+           "dit_block_set_lora", "dit_block_forward_noalloc")
 PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final", "lora")
 
 
@@ -82,6 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_block_forward.restype = ctypes.c_int
     lib.dit_block_forward_rope.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.dit_block_forward_rope.restype = ctypes.c_int
+    lib.dit_block_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    lib.dit_block_forward_noalloc.restype = ctypes.c_int
     lib.dit_qk_transform.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, vp, i64, ctypes.c_float, vp]
     lib.dit_qk_transform.restype = ctypes.c_int
     lib.dit_block_set_lora.argtypes = [vp, ctypes.POINTER(_BlockLora)]
@@ -205,6 +209,20 @@ class DitBlock:
                                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                                 _stream(stream)),
                "dit_block_forward_rope")
+        return x
+
+
+    def forward_noalloc(self, x: torch.Tensor, mod: torch.Tensor, attn_chunk_tokens: int = DEFAULT_ATTN_CHUNK,
+                        mlp_chunk_tokens: int = DEFAULT_MLP_CHUNK, ffn_chunk_features: int = 0, stream=None,
+                        rope: tuple | None = None) -> torch.Tensor:
+        """``forward`` with the library-owned static workspace (no device allocation;
+        see ``dit_block_forward_noalloc``). Raises ``DitError`` with DIT_ETOOBIG when
+        the sizes need more than ``STATIC_WORKSPACE_BYTES``."""
+        cs, sn = (None, None) if rope is None else rope
+        _check(self._lib.dit_block_forward_noalloc(self._h, x.data_ptr(), mod.data_ptr(), _ptr(cs), _ptr(sn),
+                                                   x.shape[0], attn_chunk_tokens, mlp_chunk_tokens,
+                                                   ffn_chunk_features, _stream(stream)),
+               "dit_block_forward_noalloc")
         return x
 
 

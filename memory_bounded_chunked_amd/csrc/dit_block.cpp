@@ -36,6 +36,12 @@ struct dit_block {
   dit_block_lora lora;  // rank 0 = no adapter
 };
 
+// Workspace of dit_block_forward_noalloc: one copy per GPU, loaded with the
+// library's code object and held until the process ends. In host code this
+// name is only a handle for the runtime; the device address of each GPU's
+// copy comes from hipGetSymbolAddress and is the only form host code passes on.
+static __device__ __align__(256) unsigned char scratch[DIT_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -95,6 +101,26 @@ int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chu
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_EHIP; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DIT_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return DIT_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DIT_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DIT_OK;
+}
+
 // Optional per-kernel event timing (dit_block_profile.h).
 struct Profiler {
   struct Rec {
@@ -144,6 +170,7 @@ const char* dit_block_strerror(int code) {
     case DIT_EINVAL: return "invalid argument";
     case DIT_ENOSPC: return "workspace too small";
     case DIT_EHIP: return "HIP launch error";
+    case DIT_ETOOBIG: return "sizes need more than the library's static workspace";
     default: return "unknown error";
   }
 }
@@ -488,6 +515,20 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
 #undef DIT_TRY
   (void)err;
   return DIT_OK;
+}
+
+int dit_block_forward_noalloc(dit_block* h, void* x, const float* mod, const float* rope_cos,
+                              const float* rope_sin, int64_t n_tokens, int64_t attn_chunk_tokens,
+                              int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* stream) {
+  Plan p;
+  const int rc = make_plan(h, n_tokens, attn_chunk_tokens, mlp_chunk_tokens, ffn_chunk_features, &p);
+  if (rc != DIT_OK) return rc;
+  if (p.total > DIT_STATIC_WORKSPACE_BYTES) return DIT_ETOOBIG;
+  void* ws = nullptr;
+  const int sc = scratch_of_current_device(&ws);
+  if (sc != DIT_OK) return sc;
+  return dit_block_forward_rope(h, x, mod, rope_cos, rope_sin, n_tokens, attn_chunk_tokens, mlp_chunk_tokens,
+                                ffn_chunk_features, ws, DIT_STATIC_WORKSPACE_BYTES, stream);
 }
 
 // ---------------------------------------------------------------- profiling

@@ -142,6 +142,25 @@ def test_forward_rejects_before_launch(lib):
     lib.dit_block_destroy(h)
 
 
+def test_noalloc_forward_rejects_before_any_device_call(lib):
+    # argument errors and sizes beyond the static workspace are host decisions:
+    # they return before the entry point looks up its device buffer
+    rc, h = _handle(lib)
+    assert rc == 0
+    x, mod = 0x20000, 0x30000
+    f = lib.dit_block_forward_noalloc
+    assert f(None, x, mod, None, None, 1000, 256, 256, 0, None) == B.DIT_EINVAL
+    assert f(h, x, mod, None, None, 0, 256, 256, 0, None) == B.DIT_EINVAL
+    assert f(h, x, mod, None, None, 1000, 256, 0, 0, None) == B.DIT_EINVAL
+    assert f(h, x, mod, None, None, 1000, 256, 256, 100, None) == B.DIT_EINVAL
+    n_big = 1 << 17  # d=256 bf16: global K and V alone are 128 MiB
+    _, need = _ws(lib, h, n_big, 8192, 8192, 0)
+    assert need > B.STATIC_WORKSPACE_BYTES
+    assert f(h, x, mod, None, None, n_big, 8192, 8192, 0, None) == B.DIT_ETOOBIG
+    assert B.STATIC_WORKSPACE_BYTES == 64 << 20
+    lib.dit_block_destroy(h)
+
+
 def test_step_entry_points_reject_before_launch(lib):
     p = 0x10000
     assert lib.dit_modnorm(1, 1, p, 256, p, p, p, 256, 10, 250, 1e-6, None) == B.DIT_EINVAL
