@@ -58,14 +58,34 @@ def half_ulp_bf16(a: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 9)
 
 
+# Where the widened bars come from: tests/test_tolerance.py emulates the GPU
+# path's own rounding points (n1, Q, K, V, P with the row sum of the rounded P,
+# O, n2, h, y) on the same inputs and rows as the GPU tests and checks each
+# constant below against what those roundings alone produce.
+#
+# bf16 blocks: elements above the plain 2e-2 may be at most this fraction of
+# all elements. The emulation puts at most 5e-6 of the elements of any bf16
+# test block there (1 of 198 912 on the 777-token block, 7 of 2.6 M on 512
+# rows of the 32k block); the allowance is ten times the largest, rounded up
+# to a power of ten, since an element within fp32 rounding of 2e-2 lands on
+# either side depending on summation order.
+BF16_OVER_FRACTION = 1e-4
+# The int8-weight block at full size (65 536 tokens, 512 sampled rows): the
+# emulation gives rel-L2 0.0195 on y, max-abs 0.0191 max|y_ref| and rel-L2
+# 0.0149 on O; each bar is the smallest of 2e-2, 2.5e-2, 3e-2, 4e-2, 5e-2 that
+# is at least 1.5 times its emulated value.
+INT8_BARS = {"y_rel": 3e-2, "y_max_frac": 3e-2, "o_rel": 2.5e-2}
+
+
 def check_bf16_bar(y: np.ndarray, y_ref: np.ndarray, max_abs_bar: float = 2e-2, rel_bar: float = 1e-2):
     """The bf16 parity bar: rel-L2 <= 1e-2; per element |y - y_ref| <= 2e-2 plus the
     bf16 output's own half-ulp at y_ref (x is bf16 in place, so no output can be
-    closer than that); and elements over the plain 2e-2 at most 1e-4 of all."""
+    closer than that); and elements over the plain 2e-2 at most BF16_OVER_FRACTION
+    of all."""
     err = np.abs(y - y_ref)
     assert rel_l2(y, y_ref) <= rel_bar, f"rel_l2 {rel_l2(y, y_ref)}"
     worst = float((err - half_ulp_bf16(y_ref)).max())
     assert worst <= max_abs_bar, f"max(|err| - half_ulp) = {worst}"
     over = int((err > max_abs_bar).sum())
-    assert over <= 1e-4 * err.size, f"{over} of {err.size} elements above {max_abs_bar}"
+    assert over <= BF16_OVER_FRACTION * err.size, f"{over} of {err.size} elements above {max_abs_bar}"
     return float(err.max()), over

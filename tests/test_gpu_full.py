@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle.dit_block as O
-from _helpers import check_bf16_bar, max_abs, oracle_inputs, rel_l2, to_f64
+from _helpers import INT8_BARS, check_bf16_bar, max_abs, oracle_inputs, rel_l2, to_f64
 from memory_bounded_chunked_amd import block as B
 from memory_bounded_chunked_amd import synth
 
@@ -97,12 +97,12 @@ def test_full_size_parity_and_bit_identity(name):
     if shape.dtype == "w8_bf16":
         # int8 weights (std ~0.045) push per-head logits to O(1e2): the bf16
         # rounding of norm1, Q and K that bf16 activations require moves the
-        # softmax weights by tens of percent. An fp64 emulation of exactly this
-        # block's rounding points gives rel-L2 0.017 on y; the bar is 3e-2 on y
-        # (max-abs relative to max|y_ref|) and 5e-2 on O.
-        assert rel_l2(y, y_ref) <= 3e-2
-        assert max_abs(y, y_ref) <= 3e-2 * np.abs(y_ref).max()
-        assert o_rel <= 5e-2
+        # softmax weights by tens of percent. An emulation of exactly this
+        # block's rounding points on these rows (tests/test_tolerance.py) gives
+        # rel-L2 0.0195 on y and 0.0149 on O; INT8_BARS are 1.5x those floors.
+        assert rel_l2(y, y_ref) <= INT8_BARS["y_rel"]
+        assert max_abs(y, y_ref) <= INT8_BARS["y_max_frac"] * np.abs(y_ref).max()
+        assert o_rel <= INT8_BARS["o_rel"]
     else:
         check_bf16_bar(y, y_ref)
         assert o_rel <= 1e-2
