@@ -52,6 +52,22 @@ TRAFFIC = {
         # activations + gate/up weight rows + h, bf16
         "algorithmic_bytes": (8192 * 5120 + 2 * 13824 * 5120 + 8192 * 13824) * 2,
     },
+    "modnorm": {
+        "record": "modnorm_large_8192_traffic.json",
+        "kernel": "dit::modnorm_kernel<unsigned short, unsigned short,",
+        "sources": ["memory_bounded_chunked_amd/csrc/modnorm.hip", "memory_bounded_chunked_amd/csrc/common.hpp"],
+        "workload": "norm1 of one 8192-token slab: bf16 x [8192 x 5120] -> bf16 [8192 x 5120], fp32 shift/scale",
+        # x in + normalised slab out, bf16, + shift and scale fp32
+        "algorithmic_bytes": 2 * 8192 * 5120 * 2 + 2 * 5120 * 4,
+    },
+    "norm2": {
+        "record": "norm2_large_8192_traffic.json",
+        "kernel": "dit::modnorm_kernel<float, unsigned short,",
+        "sources": ["memory_bounded_chunked_amd/csrc/modnorm.hip", "memory_bounded_chunked_amd/csrc/common.hpp"],
+        "workload": "norm2 of one 8192-token slab: fp32 staged residual [8192 x 5120] -> bf16 [8192 x 5120]",
+        # fp32 stage in + bf16 out + shift and scale fp32
+        "algorithmic_bytes": 8192 * 5120 * (4 + 2) + 2 * 5120 * 4,
+    },
     "final_layer": {
         "record": "final_layer_32k_traffic.json",
         "kernel": "dit::final_layer_kernel",
@@ -102,6 +118,14 @@ def traffic_probe(kind: str) -> int:
         w = (torch.randn(2 * f, d, device=dev, generator=g) / d ** 0.5).bfloat16()
         h = torch.empty(m, f, device=dev, dtype=torch.bfloat16)
         run = lambda: B.linear("bf16", "gateup", a_in, w, h, f, up_offset=f)  # noqa: E731
+    elif kind in ("modnorm", "norm2"):
+        m, d = 8192, 5120
+        xin = torch.randn(m, d, device=dev, generator=g)
+        if kind == "modnorm":
+            xin = xin.bfloat16()
+        sh, sc = torch.randn(d, device=dev, generator=g) * 0.3, torch.randn(d, device=dev, generator=g) * 0.3
+        out = torch.empty(m, d, device=dev, dtype=torch.bfloat16)
+        run = lambda: B.modnorm(xin, sh, sc, out)  # noqa: E731
     else:
         n, d, od = FINAL_N, FINAL_D, FINAL_OUT
         x = torch.randn(n, d, device=dev, generator=g).bfloat16()
@@ -376,6 +400,19 @@ def main() -> int:
     B.profile_enable(False)
     kernels = {k: {"total_ms_per_step": round(t / args.steps, 4), "launches_per_step": n // args.steps,
                    "avg_launch_ms": round(t / n, 4) if n else None} for k, (t, n) in prof.items()}
+    # the HBM-bound norms: algorithmic bytes of their launches (rows in, rows out,
+    # shift and scale) over their summed launch time
+    e = 4 if shape.dtype == "f32" else 2
+    n_tok, d_ = shape.n_tokens, shape.d
+    norm_bytes = {  # per forward: norm1 runs over every token twice (pass 1 and pass 2), norm2 once
+        "modnorm": 2 * n_tok * d_ * (e + e) + prof["modnorm"][1] // args.steps * 2 * d_ * 4,
+        "norm2": n_tok * d_ * (4 + e) + prof["norm2"][1] // args.steps * 2 * d_ * 4,
+    }
+    for kname, nb in norm_bytes.items():
+        t_step = kernels[kname]["total_ms_per_step"]
+        if t_step:
+            kernels[kname]["hbm_gbs"] = round(nb / (t_step / 1e3) / 1e9, 1)
+            kernels[kname]["hbm_frac"] = round(nb / (t_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
     log("[bench] per-kernel: " + json.dumps(kernels))
 
     n, d = shape.n_tokens, shape.d

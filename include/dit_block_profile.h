@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 /* Steps of the block, as tagged by the profiler. */
-#define DIT_K_MODNORM 0    /* norm1 / norm2 (modulated LayerNorm) */
+#define DIT_K_MODNORM 0    /* norm1 (modulated LayerNorm of x) */
 #define DIT_K_KV_PROJ 1    /* pass 1: K and V projections of a token slab */
 #define DIT_K_Q_PROJ 2     /* pass 2: Q projection of a slice */
 #define DIT_K_ATTENTION 3  /* pass 2: attention of a slice against global K/V */
@@ -30,7 +30,8 @@ extern "C" {
 #define DIT_K_QK 7         /* optional QK RMSNorm / RoPE of a Q or K slab */
 #define DIT_K_FINAL 8      /* dit_final_layer: the output head */
 #define DIT_K_LORA 9       /* adapter inputs t = alpha * (A a) of one launch group */
-#define DIT_K_COUNT 10
+#define DIT_K_NORM2 10     /* norm2 (modulated LayerNorm of the fp32 staged residual) */
+#define DIT_K_COUNT 11
 
 /* on != 0: clear all records and start recording; on == 0: stop recording
  * (records are kept for dit_profile_read). Returns DIT_OK. */

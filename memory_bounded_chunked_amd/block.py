@@ -31,7 +31,8 @@ EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunk
            "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
            "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer",
            "dit_block_set_lora", "dit_block_forward_noalloc")
-PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final", "lora")
+PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final", "lora",
+                 "norm2")
 
 
 class DitError(RuntimeError):

@@ -439,6 +439,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
+  // P = exp2(s * c - m * c): the exponent is one explicit fused multiply-add
+  // with m * c rounded first. settle() can run this a second time for a
+  // whole wave; spelled out, both runs give a query that did not move the
+  // same bits (left to the compiler, the second copy was contracted the
+  // other way round, and a query's P then depended on its wave-mates).
   auto exp_tile = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
     const float mc = m_run * qk_scale_log2;
     float lsum = 0.f;
@@ -449,8 +454,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[r0 + 2 * e] * qk_scale_log2 - mc);
-        const float p1 = __builtin_amdgcn_exp2f(sv[r0 + 2 * e + 1] * qk_scale_log2 - mc);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 2 * e], qk_scale_log2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 2 * e + 1], qk_scale_log2, -mc));
         w[e] = pack_bf16x2(p0, p1);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w[e]), ones, lsum, false);
       }

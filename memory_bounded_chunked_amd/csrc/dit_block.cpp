@@ -462,7 +462,7 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       float* srows = stage + (m0 - t0) * d;
       char* n2 = slab_a;
       char* hbuf = slab_a + round_up((size_t)p.cm * d * e, kAlign);
-      DIT_TRY(DIT_K_MODNORM, launch_modnorm(1, f32, srows, d, sh2, sc2, n2, d, c, (int)d, dsc.eps, st));
+      DIT_TRY(DIT_K_NORM2, launch_modnorm(1, f32, srows, d, sh2, sc2, n2, d, c, (int)d, dsc.eps, st));
       // adapter inputs of this slab: [gate | up | down] columns of one t
       const int64_t ldt_m = rk.mlp();
       if (lo.gate.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.gate, n2, d, c, d, 0, d, ldt_m, 0, 0));

@@ -785,10 +785,10 @@ static int64_t wide_split(int64_t m, int64_t n, int cus, int64_t wb) {
 
 template <typename TA, typename TB, int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  // The tile shapes depend only on M, N and the epilogue, and which tile
-  // computes an element does not change its value (every tile shape runs the
-  // same k sequence), so every token row gets the same bits whatever the slab
-  // size. 8 wavefronts (2 per SIMD) per 256-row tile: while one wave waits on
+  // The tile shapes depend on M, N, the epilogue and the compute-unit count,
+  // but which tile computes an element does not change its value (every tile
+  // shape runs the same MFMA over the same k sequence), so every token row
+  // gets the same bits whatever the slab size. 8 wavefronts (2 per SIMD) per 256-row tile: while one wave waits on
   // LDS or a barrier, the other keeps the matrix core busy.
   if constexpr (EPI == EPI_KV || EPI == EPI_LORA_T) {
     if (g.N % 256 == 0 && g.N >= 8192) return launch_tile<TA, TB, EPI, 256, 2, 4>(g, st);

@@ -38,7 +38,8 @@ import numpy as np
 __all__ = [
     "layer_norm", "modulate", "linear", "silu", "attention", "dequantize_rows",
     "rms_norm_heads", "rope", "qk_transform", "final_layer", "final_layer_chunked",
-    "lora_delta", "lora_f64", "block_weights_f64", "block_forward", "block_forward_chunked", "block_rows",
+    "lora_delta", "lora_f64", "block_weights_f64", "block_forward", "block_forward_chunked", "global_kv",
+    "block_rows",
 ]
 
 # Projections an adapter can attach to, in the block's own names.
@@ -335,26 +336,39 @@ def block_forward_chunked(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int,
     return res
 
 
+def global_kv(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, eps: float = 1e-6,
+              qk: dict | None = None, lora: dict | None = None) -> tuple:
+    """K and V of all N tokens (K after its QK transform, if any): what every
+    query row attends to."""
+    d = x.shape[1]
+    _, wk, wv = _split(w, d)
+    qk = qk or {}
+    lo = lora or {}
+    n1_all = modulate(layer_norm(x, eps), np.asarray(mod[0], np.float64), np.asarray(mod[1], np.float64))
+    k = linear(n1_all, wk) + lora_delta(n1_all, lo.get("k"))
+    v = linear(n1_all, wv) + lora_delta(n1_all, lo.get("v"))
+    del n1_all
+    k = qk_transform(k, qk.get("k_norm"), qk.get("cos"), qk.get("sin"), n_heads, eps)
+    return k, v
+
+
 def block_rows(x: np.ndarray, mod: np.ndarray, w: dict, n_heads: int, rows: np.ndarray,
                eps: float = 1e-6, want: tuple = (), qk: dict | None = None,
-               lora: dict | None = None) -> np.ndarray | tuple:
+               lora: dict | None = None, kv: tuple | None = None) -> np.ndarray | tuple:
     """The block output for the query rows ``rows`` only (exact for those rows).
 
     norm1 and K/V are computed for all N tokens, because every query attends
-    every key; every later step is per token, so it runs on the chosen rows.
+    every key (``global_kv``; ``kv`` passes them in when several row sets share
+    them); every later step is per token, so it runs on the chosen rows.
     """
     d = x.shape[1]
     ffn = w["down"].shape[1]
     sh1, sc1, g1, sh2, sc2, g2 = (np.asarray(m, np.float64) for m in mod)
-    wq, wk, wv = _split(w, d)
+    wq, _, _ = _split(w, d)
     qk = qk or {}
     lo = lora or {}
     cos, sin = qk.get("cos"), qk.get("sin")
-    n1_all = modulate(layer_norm(x, eps), sh1, sc1)
-    k = linear(n1_all, wk) + lora_delta(n1_all, lo.get("k"))
-    v = linear(n1_all, wv) + lora_delta(n1_all, lo.get("v"))
-    del n1_all
-    k = qk_transform(k, qk.get("k_norm"), cos, sin, n_heads, eps)
+    k, v = global_kv(x, mod, w, n_heads, eps, qk, lora) if kv is None else kv
     xr = x[rows]
     n1 = modulate(layer_norm(xr, eps), sh1, sc1)
     q = qk_transform(linear(n1, wq) + lora_delta(n1, lo.get("q")), qk.get("q_norm"),

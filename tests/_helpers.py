@@ -72,9 +72,19 @@ def half_ulp_bf16(a: np.ndarray) -> np.ndarray:
 BF16_OVER_FRACTION = 1e-4
 # The int8-weight block at full size (65 536 tokens, 512 sampled rows): the
 # emulation gives rel-L2 0.0195 on y, max-abs 0.0191 max|y_ref| and rel-L2
-# 0.0149 on O; each bar is the smallest of 2e-2, 2.5e-2, 3e-2, 4e-2, 5e-2 that
-# is at least 1.5 times its emulated value.
+# 0.0149 on O; each bar is the smallest step of BAR_LADDER that is at least
+# 1.5 times its emulated value.
+BAR_LADDER = (5e-3, 1e-2, 2e-2, 2.5e-2, 3e-2, 4e-2, 5e-2)
 INT8_BARS = {"y_rel": 3e-2, "y_max_frac": 3e-2, "o_rel": 2.5e-2}
+# int8 weights with rank-80 and rank-256 adapters in the 256-wide weight tiles
+# (the kernels whose adapter phase follows the main loop): |y| reaches 25 (d =
+# 1024) and 70 (d = 4096), so the bars are relative, derived like INT8_BARS
+# from the emulated floors (the larger of the two ranks): d = 1024 rel-L2
+# 0.0032 on y and max-abs 0.0045 max|y_ref|; d = 4096 0.0137 and 0.0203.
+INT8_ADAPTER_SHAPES = {
+    "i8-wide": ((1024, 8, 128, 4096, 16384), {"y_rel": 5e-3, "y_max_frac": 1e-2}),
+    "i8-kv256": ((4096, 32, 128, 2048, 1024), {"y_rel": 2.5e-2, "y_max_frac": 4e-2}),
+}
 
 
 def check_bf16_bar(y: np.ndarray, y_ref: np.ndarray, max_abs_bar: float = 2e-2, rel_bar: float = 1e-2):

@@ -21,9 +21,14 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "memory_bounded_chunked_amd", "libdit_block.so")
 LLVM = "/opt/rocm/llvm/bin"
+# The int8 256x256 kernels with the adapter phase, by epilogue: the spill
+# counts of the current build (the phase runs after the main loop; the
+# register-heavy ones are the SwiGLU and the K|V epilogues). A change in the
+# kernel that spills more fails here and has to be looked at.
+INT8_ADAPTER_SPILLS = {0: 85, 1: 84, 2: 83, 3: 190, 4: 83, 5: 83, 6: 183}
 ALLOWED = {  # kernel: most spilled VGPRs allowed
-    **{f"_ZN3dit11gemm_kernelItaLi{epi}ELi256ELi256ELi2ELi4ELb1EEEvNS_8GemmArgsE": 1 << 30  # int8, adapter phase
-       for epi in range(7)},
+    **{f"_ZN3dit11gemm_kernelItaLi{epi}ELi256ELi256ELi2ELi4ELb1EEEvNS_8GemmArgsE": n
+       for epi, n in INT8_ADAPTER_SPILLS.items()},
     "_ZN3dit21attention_bf16_kernelILi128EEEvPKtlS2_lS2_lPtlllf": 8,  # outside the key loop
 }
 

@@ -11,6 +11,8 @@ keys and checked directly, because its contribution to y sits near the bf16
 resolution of y.
 """
 import hashlib
+import sys
+import time
 
 import numpy as np
 import pytest
@@ -137,3 +139,30 @@ def test_full_size_with_qk_norm_and_rope():
     y = to_f64(y_first[torch.from_numpy(rows)])
     print(f"\nlarge+qk: y max_abs={max_abs(y, y_ref):.4g} rel_l2={rel_l2(y, y_ref):.4g}")
     check_bf16_bar(y, y_ref)
+
+
+def test_mid_block_full_parity():
+    # Every one of the 16384 x 3072 outputs of the mid block (bench chunking
+    # 4096 / 4096) against the oracle: global K/V once, then the rows in slabs
+    # of 4096 (the oracle takes about two minutes on 16 host cores; a line per
+    # step goes to the terminal).
+    shape = synth.CONFIGS["mid"]
+    n = shape.n_tokens
+    inputs = synth.make_inputs(shape, seed=0)
+    blk, x0, mod = B.block_from_inputs(shape, inputs, "cuda")
+    y_gpu = to_f64(_forward(blk, x0, mod, n, shape.attn_chunk, shape.mlp_chunk, 0).cpu())
+    blk.close()
+    del x0
+    torch.cuda.empty_cache()
+    x, modf, w = oracle_inputs(inputs)
+    t0 = time.time()
+    kv = O.global_kv(x, modf, w, shape.n_heads, eps=shape.eps)
+    print(f"[mid full] oracle K/V of {n} tokens: {time.time() - t0:.0f} s", file=sys.__stderr__, flush=True)
+    y_ref = np.empty_like(x)
+    for r0 in range(0, n, 4096):
+        rows = np.arange(r0, min(n, r0 + 4096))
+        y_ref[rows] = O.block_rows(x, modf, w, shape.n_heads, rows, eps=shape.eps, kv=kv)
+        print(f"[mid full] oracle rows {r0}-{rows[-1]}: {time.time() - t0:.0f} s", file=sys.__stderr__, flush=True)
+    print(f"\nmid full: y max_abs={max_abs(y_gpu, y_ref):.4g} rel_l2={rel_l2(y_gpu, y_ref):.4g} "
+          f"elements over 2e-2: {int((np.abs(y_gpu - y_ref) > 2e-2).sum())} of {y_ref.size}")
+    check_bf16_bar(y_gpu, y_ref)

@@ -99,17 +99,37 @@ def test_linear_store(dtype, m, n, k):
     assert np.all(np.abs(to_f64(out) - ref) <= np.abs(ref) * _out_tol(dtype) + 1e-5 * scale)
 
 
+def _wide_columns(m: int, n: int, wb: int = 256, cus: int = 256) -> int:
+    """Output columns the projection launcher gives 256-wide weight tiles (the
+    rest take 128-wide ones): the split that fills whole rounds of the compute
+    units, one round of 128-wide tiles costing 0.6 of a 256-wide round."""
+    mt = -(-m // 256)
+    best, na_best = None, 0
+    for na in range(0, n + 1, wb):
+        c = -(-mt * (na // wb) // cus) + 0.6 * -(-mt * ((n - na) // (wb // 2)) // cus)
+        if best is None or c <= best:
+            best, na_best = c, na
+    return na_best
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
 def test_linear_tile_shape_does_not_change_bits(dtype):
-    # The same output columns through launches that pick different tiles (256
-    # or 128 or 64 weight rows per tile; 8 waves in two groups, or 4 waves):
-    # every element takes the same k sequence, so the bits must agree. The
-    # block's bit-identity across chunk sizes relies on this.
-    m, n, k = 300, 2048, 512
+    # The same output columns through launches that pick different tiles: the
+    # full launch runs every column in 256-wide weight tiles (8 waves, 2 x 4;
+    # the two-group schedule for bf16 weights), the slices in 128-wide (4 x 2
+    # waves) and 64-wide (4 waves) ones. Every element takes the same k
+    # sequence, so the bits must agree; the block's bit-identity across chunk
+    # sizes relies on this.
+    m, n, k = 16384, 1024, 512
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("tile choice below assumes 256 compute units")
+    assert _wide_columns(m, n) == n  # the full launch: 256-wide tiles only
     a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 21)
     full = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
     B.linear(dtype, "store", ta, tw, full, n, w_scale=ts)
-    for c0, width in ((0, 64), (64, 128), (256, 256), (512, 1536), (1984, 64)):
+    for c0, width in ((0, 64), (64, 128), (256, 256), (512, 512), (960, 64)):
+        if width >= 128:
+            assert _wide_columns(m, width) == 0  # 128-wide tiles only
         part = torch.empty(m, width, dtype=_act_dtype(dtype), device=DEV)
         B.linear(dtype, "store", ta, tw[c0:c0 + width], part, width, w_scale=None if ts is None else ts[c0:c0 + width])
         torch.cuda.synchronize()
@@ -285,3 +305,35 @@ def test_qk_transform(dtype, heads, dh, rows, mode):
     got = to_f64(x)
     tol = 1e-5 if dtype == "f32" else 2.0 ** -8
     assert np.all(np.abs(got - ref) <= np.abs(ref) * tol + tol * 1e-2 * np.abs(ref).max())
+
+
+def test_attention_query_independent_of_wave_mates_with_moving_maxima():
+    # Q, K and V^T of an int8-weight block (d = 4096, 32 heads x 128, 1024
+    # tokens) through the step kernels: per-head logits reach tens of units,
+    # so running maxima move in later key tiles for some queries of a
+    # wavefront and not for others, and a wave whose query moves exponentiates
+    # its tile again. A query's O must not depend on the queries that share its
+    # wavefront: slices starting at offsets that are not multiples of 32, and
+    # single rows, must give the bits of the full launch (with the second
+    # exponentiation compiled differently from the first, query 296 of head 23
+    # did not).
+    shape = synth.BlockShape("att-mates", 4096, 32, 128, 2048, 1024, "w8_bf16")
+    inp = synth.make_inputs(shape, 0)
+    t = {k: B.tensor_from_stored(v, DEV) for k, v in inp.items()}
+    n, d = shape.n_tokens, shape.d
+    w, sc = t["w_qkv"], t["s_qkv"]
+    n1 = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    B.modnorm(t["x"], t["mod"][0], t["mod"][1], n1)
+    q = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    vt = torch.zeros(d, n, dtype=torch.bfloat16, device=DEV)
+    B.linear("w8_bf16", "store", n1, w[:d], q, d, w_scale=sc[:d])
+    B.linear("w8_bf16", "store", n1, w[d:2 * d], k, d, w_scale=sc[d:2 * d])
+    B.linear("w8_bf16", "store_t", n1, w[2 * d:], vt, d, w_scale=sc[2 * d:])
+    full = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    B.attention(q, k, vt, full, shape.n_heads)
+    for s0, c in ((0, 300), (300, 300), (600, 300), (200, 100), (5, 1019), (296, 1), (567, 1)):
+        part = torch.empty(c, d, dtype=torch.bfloat16, device=DEV)
+        B.attention(q[s0:s0 + c].contiguous(), k, vt, part, shape.n_heads)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu(), full[s0:s0 + c].cpu()), (s0, c)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle.dit_block as O
-from _helpers import bits, check_bf16_bar, half_ulp_bf16, max_abs, oracle_inputs, rel_l2, to_f64
+from _helpers import INT8_ADAPTER_SHAPES, bits, check_bf16_bar, half_ulp_bf16, max_abs, oracle_inputs, rel_l2, to_f64
 from memory_bounded_chunked_amd import block as B
 from memory_bounded_chunked_amd import synth
 
@@ -190,3 +190,34 @@ def test_lora_mid_block_sampled_rows():
     y_ref = O.block_rows(x, mod, w, shape.n_heads, rows, lora=_lora_f64(lora))
     check_bf16_bar(to_f64(y)[rows], y_ref)
     assert bits(_run(shape, inputs, lora, 0, shape.n_tokens)) == bits(y)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(INT8_ADAPTER_SHAPES))
+@pytest.mark.parametrize("rank", [80, 256])
+def test_int8_adapters_in_wide_tiles(name, rank):
+    # int8 weights with adapters where the projections take 256-wide weight
+    # tiles, whose adapter phase runs after the main loop (with all
+    # accumulators live; LDS-staged in batches of 4 loads). d = 1024 with 16384
+    # tokens: the Q, out, gate/up, down and feature-slice (ACCUM) projections
+    # of a 16384-token slab run in 256-wide tiles, those of 4096-token slabs in
+    # 128-wide ones; d = 4096: the fused K|V projection (2d = 8192 outputs)
+    # runs in 256-wide tiles. Ranks 80 (a ragged second staging chunk) and 256
+    # (four chunks). Against the oracle on 512 sampled rows with the bars that
+    # the emulation of the path's rounding points derives (INT8_ADAPTER_SHAPES),
+    # and bit-identical across chunk settings.
+    (d, heads, dh, ffn, n), bars = INT8_ADAPTER_SHAPES[name]
+    shape = synth.BlockShape(name, d, heads, dh, ffn, n, "w8_bf16")
+    inputs = synth.make_inputs(shape, seed=0)
+    lora = synth.make_lora(shape, rank, seed=3)
+    sweep = [(n, n, 0), (n // 4, n // 4, 0), (0, 5000, 0)] if n >= 16384 else [(n, n, 0), (300, 500, 0), (100, 64, 0)]
+    outs = [_run(shape, inputs, lora, ca, cm, fc) for ca, cm, fc in sweep]
+    assert all(bits(o) == bits(outs[0]) for o in outs[1:]), "bit-identity across (Ca, Cm)"
+    sliced = _run(shape, inputs, lora, n, n, ffn // 2)  # two FFN feature slices: EPI_ACCUM then EPI_FINAL
+    rows = synth.sample_rows(n, 512)
+    x, mod, w = oracle_inputs(inputs)
+    y_ref = O.block_rows(x, mod, w, heads, rows, lora=_lora_f64(lora))
+    for out in (outs[0], sliced):
+        y = to_f64(out)[rows]
+        assert rel_l2(y, y_ref) <= bars["y_rel"], rel_l2(y, y_ref)
+        assert max_abs(y, y_ref) <= bars["y_max_frac"] * np.abs(y_ref).max(), max_abs(y, y_ref)

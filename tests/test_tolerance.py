@@ -21,7 +21,8 @@ import pytest
 import torch
 
 import oracle.dit_block as O
-from _helpers import BF16_OVER_FRACTION, INT8_BARS, half_ulp_bf16, oracle_inputs, rel_l2
+from _helpers import (BAR_LADDER, BF16_OVER_FRACTION, INT8_ADAPTER_SHAPES, INT8_BARS, half_ulp_bf16, oracle_inputs,
+                      rel_l2)
 from memory_bounded_chunked_amd import synth
 
 R = lambda a: synth.bf16_bits_to_f64(synth.f64_to_bf16_bits(a))  # noqa: E731
@@ -108,22 +109,29 @@ def _modnorm32(x, shift, scale, eps):
     return _r(xc * torch.rsqrt(var + eps) * (1 + scale) + shift)
 
 
-def emulate_rows(inputs: dict, shape, rows: np.ndarray, eps: float = 1e-6):
-    """(y, O) of the sampled ``rows`` through the GPU path's rounding points, fp32 between them."""
+def emulate_rows(inputs: dict, shape, rows: np.ndarray, eps: float = 1e-6, lora: dict | None = None):
+    """(y, O) of the sampled ``rows`` through the GPU path's rounding points, fp32 between them.
+    ``lora``: {target: (A, B, alpha)} stored adapters; t = alpha (A a) stays unrounded and
+    B t joins the projection's sum (after the per-row scale of int8 weights)."""
     d, f, heads = shape.d, shape.ffn, shape.n_heads
     dh = d // heads
     mod = torch.from_numpy(inputs["mod"])
+    lo = {k: (_t32(a), _t32(b), al) for k, (a, b, al) in (lora or {}).items()}
 
-    def weight(name, r0, r1):
+    def weight(name, r0, r1, target=None):
         s = inputs.get("s_" + name)
-        return _t32(inputs["w_" + name][r0:r1]), None if s is None else torch.from_numpy(s[r0:r1])
+        return _t32(inputs["w_" + name][r0:r1]), None if s is None else torch.from_numpy(s[r0:r1]), target
 
     def proj(a, w):
         y = a @ w[0].T
-        return y if w[1] is None else y * w[1]
+        y = y if w[1] is None else y * w[1]
+        if w[2] in lo:
+            a_m, b_m, alpha = lo[w[2]]
+            y = y + (alpha * (a @ a_m.T)) @ b_m.T
+        return y
 
     n = shape.n_tokens
-    wk, wv = weight("qkv", d, 2 * d), weight("qkv", 2 * d, 3 * d)
+    wk, wv = weight("qkv", d, 2 * d, "k"), weight("qkv", 2 * d, 3 * d, "v")
     kh = torch.empty(heads, n, dh)
     vh = torch.empty(heads, n, dh)
     for r0 in range(0, n, 8192):
@@ -132,7 +140,7 @@ def emulate_rows(inputs: dict, shape, rows: np.ndarray, eps: float = 1e-6):
         vh[:, r0:r0 + 8192] = _r(proj(n1, wv)).view(-1, heads, dh).transpose(0, 1)
     del wk, wv
     xr = _t32(inputs["x"][rows])
-    q = _r(proj(_modnorm32(xr, mod[0], mod[1], eps), weight("qkv", 0, d))).view(-1, heads, dh).transpose(0, 1)
+    q = _r(proj(_modnorm32(xr, mod[0], mod[1], eps), weight("qkv", 0, d, "q"))).view(-1, heads, dh).transpose(0, 1)
     o = torch.empty(heads, len(rows), dh)
     for h in range(heads):
         s = (q[h] @ kh[h].T) / float(np.sqrt(dh))
@@ -140,10 +148,10 @@ def emulate_rows(inputs: dict, shape, rows: np.ndarray, eps: float = 1e-6):
         o[h] = (p @ vh[h]) / p.sum(1, keepdim=True)
     del kh, vh
     o = _r(o.transpose(0, 1).reshape(-1, d))
-    x1 = xr + mod[2] * proj(o, weight("o", 0, d))
+    x1 = xr + mod[2] * proj(o, weight("o", 0, d, "o"))
     n2 = _modnorm32(x1, mod[3], mod[4], eps)
-    hh = _r(torch.nn.functional.silu(proj(n2, weight("gu", 0, f))) * proj(n2, weight("gu", f, 2 * f)))
-    y = _r(x1 + mod[5] * proj(hh, weight("down", 0, d)))
+    hh = _r(torch.nn.functional.silu(proj(n2, weight("gu", 0, f, "gate"))) * proj(n2, weight("gu", f, 2 * f, "up")))
+    y = _r(x1 + mod[5] * proj(hh, weight("down", 0, d, "down")))
     return y.double().numpy(), o.double().numpy()
 
 
@@ -220,7 +228,12 @@ def test_bf16_bar_at_the_32k_block():
 
 
 def _bar_for(floor: float) -> float:
-    return min(b for b in (2e-2, 2.5e-2, 3e-2, 4e-2, 5e-2) if b >= 1.5 * floor)
+    return min(b for b in BAR_LADDER if b >= 1.5 * floor)
+
+
+def _int8_floors(y, o, y_ref, o_ref) -> dict:
+    return {"y_rel": rel_l2(y, y_ref), "y_max_frac": float(np.abs(y - y_ref).max() / np.abs(y_ref).max()),
+            "o_rel": rel_l2(o, o_ref)}
 
 
 @pytest.mark.slow
@@ -232,9 +245,32 @@ def test_int8_bar_at_full_size():
     shape = synth.CONFIGS["int8"]
     rows = synth.sample_rows(shape.n_tokens, 512)
     y, o, y_ref, o_ref = _oracle_then_emulation(shape, rows)
-    floors = {"y_rel": rel_l2(y, y_ref), "y_max_frac": float(np.abs(y - y_ref).max() / np.abs(y_ref).max()),
-              "o_rel": rel_l2(o, o_ref)}
+    floors = _int8_floors(y, o, y_ref, o_ref)
     print("int8 emulated floors:", {k: round(v, 5) for k, v in floors.items()})
     assert 1e-2 < floors["y_rel"] < 2.5e-2
     for key, floor in floors.items():
         assert INT8_BARS[key] == _bar_for(floor), (key, floor)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(INT8_ADAPTER_SHAPES))
+def test_int8_adapter_bars(name):
+    # the GPU test of int8 weights with adapters in the 256-wide weight tiles:
+    # its bars are derived from the emulated floors at ranks 80 and 256, on
+    # its own inputs (adapters from seed 3) and 512 sampled rows
+    (d, heads, dh, ffn, n), bars = INT8_ADAPTER_SHAPES[name]
+    shape = synth.BlockShape(name, d, heads, dh, ffn, n, "w8_bf16")
+    inputs = synth.make_inputs(shape, seed=0)
+    rows = synth.sample_rows(n, 512)
+    x, mod, w = oracle_inputs(inputs)
+    worst = {}
+    for rank in (80, 256):
+        lora = synth.make_lora(shape, rank, seed=3)
+        lf = O.lora_f64({k: (synth.to_f64(a), synth.to_f64(b), al) for k, (a, b, al) in lora.items()})
+        y_ref, o_ref = O.block_rows(x, mod, w, heads, rows, want=("o",), lora=lf)
+        y, o = emulate_rows(inputs, shape, rows, lora=lora)
+        for key, v in _int8_floors(y, o, y_ref, o_ref).items():
+            worst[key] = max(worst.get(key, 0.0), v)
+    print(f"\n{name} emulated floors:", {k: round(v, 5) for k, v in worst.items()})
+    for key, bar in bars.items():
+        assert bar == _bar_for(worst[key]), (key, worst[key])
