@@ -317,6 +317,8 @@ def main() -> int:
     ap.add_argument("--attn-chunk", type=int, default=None)
     ap.add_argument("--mlp-chunk", type=int, default=None)
     ap.add_argument("--ffn-chunk", type=int, default=None)
+    ap.add_argument("--attn-splits", type=int, default=1,
+                    help="key ranges per query in attention (dit_block_set_attention_splits)")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk", action="store_true", help="with QK RMSNorm and RoPE (a widening of the path)")
@@ -359,6 +361,8 @@ def main() -> int:
         inputs = {**inputs, "q_norm": qk_in["q_norm"], "k_norm": qk_in["k_norm"]}
         rope = (torch.from_numpy(qk_in["cos"]).to(dev), torch.from_numpy(qk_in["sin"]).to(dev))
     blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
+    if args.attn_splits != 1:
+        blk.set_attention_splits(args.attn_splits)
     lora_flops = 0.0
     if args.lora:
         lora = synth.make_lora(shape, args.lora, seed=0)
@@ -433,7 +437,8 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(att_tflops / peak, 4) if att_tflops else None,
-        "traffic": (measured_traffic("attention") if args.config == "large" and ca == 8192 else None),
+        "traffic": (measured_traffic("attention") if args.config == "large" and ca == 8192 and args.attn_splits == 1
+                    else None),
         "avg_launch_ms": round(att_avg_ms, 4) if att_avg_ms else None,
         "flops_per_launch": att_flops_launch,
     }
@@ -456,6 +461,7 @@ def main() -> int:
                          + (", QK RMSNorm + RoPE" if args.qk else "")
                          + (f", rank-{args.lora} adapters on q/k/v/o/gate/up/down" if args.lora else "")),
             "n_tokens": n, "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
+            **({"attention_splits": args.attn_splits} if args.attn_splits != 1 else {}),
             "peak_workspace_bytes": ws_bytes,
             "tflops": round(tflops, 1),
             "frac_bf16_peak": round(tflops / peak, 4),

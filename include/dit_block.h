@@ -109,6 +109,9 @@ int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit
  *   + d*Np*e          global V, stored transposed [d][Np]
  *   + S*d*4           fp32 residual staging for one super-slice
  *   + max(2*Ca*d*e, Cm*d*e + Cm*fc*e)    slabs: norm/O + Q, or norm2 + h
+ *   + (S > 1 only) S*Ca*d*4 + S*Ca*H*2*4 the key ranges' partial O, m and l
+ *     (S = min(attention splits, ceil(N/64)), H = n_heads; see
+ *     dit_block_set_attention_splits)
  * Only the K/V terms grow with N ("Where people get burned": K and V for the
  * whole sequence stay resident and set the memory floor). Same argument
  * rules and errors as dit_block_forward. */
@@ -201,6 +204,20 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
 int dit_block_forward_noalloc(dit_block* h, void* x, const float* mod, const float* rope_cos,
                               const float* rope_sin, int64_t n_tokens, int64_t attn_chunk_tokens,
                               int64_t mlp_chunk_tokens, int64_t ffn_chunk_features, void* stream);
+
+/* Key ranges per query in the attention of this handle's forwards (default
+ * 1). With splits > 1 every query's keys are cut into S = min(splits,
+ * ceil(N/64)) contiguous ranges of 64-key tiles, attended by separate
+ * workgroups and merged in a fixed order (dit_attention_split), so a short
+ * attention slice (small attn_chunk_tokens) still fills the GPU: an
+ * attention launch has ceil(Ca/256) * n_heads * S workgroups. The cut
+ * depends only on N and splits, so the output bytes are still identical for
+ * every (attn_chunk_tokens, mlp_chunk_tokens) at a fixed splits; across
+ * different splits they agree within rounding. The workspace grows by the
+ * partials' S*Ca*d*4 + S*Ca*H*8 bytes (dit_block_peak_workspace).
+ * Host metadata only. Errors: DIT_EINVAL for a null handle or splits
+ * outside 1..64. */
+int dit_block_set_attention_splits(dit_block* h, int64_t splits);
 
 /* One activation-space adapter ("ComfyUI-StaticPipeline", section
  * "Activation-space LoRA (bypass mode)"): a projection y = W a of the block

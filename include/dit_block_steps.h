@@ -51,6 +51,32 @@ int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int6
                   const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv,
                   int64_t n_heads, int64_t head_dim, void* stream);
 
+/* dit_attention with each query's keys cut into contiguous ranges that
+ * separate workgroups attend, merged afterwards: more workgroups for short
+ * query slices. Range p of S = min(splits, ceil(n_kv/64)) is key tiles
+ * [p*T/S, (p+1)*T/S) of the T = ceil(n_kv/64) 64-key tiles (the cut depends
+ * only on n_kv and splits, never on the query rows). Each range's
+ * unnormalised fp32 O, running max m and row sum l go to the workspace; a
+ * second kernel forms O = (sum_p w_p O_p) / (sum_p w_p l_p) with
+ * w_p = exp2((m_p - max_p m_p) * log2(e) / sqrt(head_dim)), p in order.
+ * The result is within rounding of dit_attention (splits = 1 is
+ * dit_attention exactly), and a query's bits do not depend on the other
+ * query rows of the call.
+ * workspace: at least dit_attention_split_workspace() bytes, 16-byte aligned,
+ * device memory owned by the caller (unused when S = 1).
+ * Other arguments and errors as dit_attention; splits outside 1..64 is
+ * DIT_EINVAL, a smaller workspace DIT_ENOSPC. */
+int dit_attention_split(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                        const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv,
+                        int64_t n_heads, int64_t head_dim, int64_t splits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of dit_attention_split (host arithmetic): with S as there
+ * and d = n_heads*head_dim, 0 when S = 1, else
+ *   round_up(S*n_q*d*4, 256) + round_up(S*n_q*n_heads*2*4, 256). */
+int dit_attention_split_workspace(int64_t n_q, int64_t n_kv, int64_t n_heads, int64_t head_dim, int64_t splits,
+                                  size_t* bytes_out);
+
 /* QK RMSNorm and/or RoPE in place on `rows` token rows (the Q normalization /
  * positional transform of the streamed-Q plan, "Attention requires a stronger
  * contract" of the streaming proposal):

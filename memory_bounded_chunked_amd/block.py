@@ -30,7 +30,8 @@ DEFAULT_MLP_CHUNK = 8192
 EXPORTS = ("dit_block_create", "dit_block_peak_workspace", "dit_block_plan_chunks", "dit_block_forward",
            "dit_block_forward_rope", "dit_block_destroy", "dit_block_strerror", "dit_modnorm", "dit_attention",
            "dit_qk_transform", "dit_linear", "dit_profile_enable", "dit_profile_read", "dit_final_layer",
-           "dit_block_set_lora", "dit_block_forward_noalloc")
+           "dit_block_set_lora", "dit_block_forward_noalloc", "dit_block_set_attention_splits",
+           "dit_attention_split", "dit_attention_split_workspace")
 PROFILE_KINDS = ("modnorm", "kv_proj", "q_proj", "attention", "out_proj", "gate_up", "down", "qk", "final", "lora",
                  "norm2")
 
@@ -87,6 +88,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dit_block_forward_rope.restype = ctypes.c_int
     lib.dit_block_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     lib.dit_block_forward_noalloc.restype = ctypes.c_int
+    lib.dit_block_set_attention_splits.argtypes = [vp, i64]
+    lib.dit_block_set_attention_splits.restype = ctypes.c_int
+    lib.dit_attention_split.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, i64, vp,
+                                        ctypes.c_size_t, vp]
+    lib.dit_attention_split.restype = ctypes.c_int
+    lib.dit_attention_split_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dit_attention_split_workspace.restype = ctypes.c_int
     lib.dit_qk_transform.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, vp, i64, ctypes.c_float, vp]
     lib.dit_qk_transform.restype = ctypes.c_int
     lib.dit_block_set_lora.argtypes = [vp, ctypes.POINTER(_BlockLora)]
@@ -170,6 +178,11 @@ class DitBlock:
             setattr(st, name, _Lora(a.data_ptr(), b.data_ptr(), a.shape[0], float(alpha)))
         _check(self._lib.dit_block_set_lora(self._h, ctypes.byref(st)), "dit_block_set_lora")
         self._lora = dict(adapters)
+
+    def set_attention_splits(self, splits: int) -> None:
+        """Key ranges per query in this block's attention (see
+        ``dit_block_set_attention_splits``); 1 = none."""
+        _check(self._lib.dit_block_set_attention_splits(self._h, splits), "dit_block_set_attention_splits")
 
     def close(self) -> None:
         if getattr(self, "_h", None):
@@ -260,6 +273,27 @@ def attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Ten
     _check(lib.dit_attention(dt, q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(),
                              vt.stride(0), out.data_ptr(), out.stride(0), q.shape[0], n_kv, n_heads, head_dim,
                              _stream(stream)), "dit_attention")
+    return out
+
+
+def attention_split(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, n_heads: int,
+                    splits: int, n_kv: int | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Attention with each query's keys in ``splits`` ranges merged afterwards
+    (two kernels; see ``dit_attention_split``)."""
+    lib = load_library()
+    dt = {torch.float32: 0, torch.bfloat16: 1}[q.dtype]
+    n_kv = k.shape[0] if n_kv is None else n_kv
+    head_dim = q.shape[1] // n_heads
+    need = ctypes.c_size_t()
+    _check(lib.dit_attention_split_workspace(q.shape[0], n_kv, n_heads, head_dim, splits, ctypes.byref(need)),
+           "dit_attention_split_workspace")
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.dit_attention_split(dt, q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(),
+                                   vt.stride(0), out.data_ptr(), out.stride(0), q.shape[0], n_kv, n_heads, head_dim,
+                                   splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "dit_attention_split")
     return out
 
 

@@ -30,6 +30,23 @@ namespace dit {
 
 constexpr int ATT_BN = 64;  // keys per tile
 
+// Key split: the keys of every query are cut into `splits` contiguous ranges
+// of whole 64-key tiles, range p = tiles [p*T/splits, (p+1)*T/splits) of the
+// T = ceil(n_kv/64) tiles. The cut depends only on n_kv and splits. With
+// splits > 1 each workgroup attends one range and writes, per query and head,
+// its unnormalised fp32 O and its (running max m, row sum l); the combine
+// kernel merges the ranges in order p = 0, 1, ...
+struct AttSplit {
+  int splits;        // 1: no split (O written normalised, in the output type)
+  float* o_part;     // [splits][n_q][d] unnormalised O of each range (splits > 1)
+  float* ml_part;    // [splits][n_q][n_heads][2]: m (in score units) and l of each range
+};
+
+__device__ __forceinline__ void key_range(int64_t n_tiles, int splits, int p, int64_t& kt0, int64_t& kt1) {
+  kt0 = (int64_t)p * n_tiles / splits;
+  kt1 = (int64_t)(p + 1) * n_tiles / splits;
+}
+
 template <typename T, int DH, int NW>
 struct AttLayout {
   static constexpr bool F32 = sizeof(T) == 4;
@@ -48,12 +65,12 @@ struct AttLayout {
   static_assert(ATT_BN * KCH % NTHR == 0 && DH * VCH % NTHR == 0, "tile loads");
 };
 
-template <typename T, int DH, int NW>
+template <typename T, int DH, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict__ q, int64_t ldq,
                                                             const T* __restrict__ k, int64_t ldk,
                                                             const T* __restrict__ vt, int64_t ldvt,
                                                             T* __restrict__ o, int64_t ldo, int64_t n_q,
-                                                            int64_t n_kv, float qk_scale_log2) {
+                                                            int64_t n_kv, float qk_scale_log2, AttSplit sp) {
   using L = AttLayout<T, DH, NW>;
   constexpr bool F32 = L::F32;
   constexpr int EPC = L::EPC, KCH = L::KCH, VCH = L::VCH, KRP = L::KRP, VRP = L::VRP;
@@ -243,33 +260,57 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
     }
   };
 
-  // Full tiles in the loop (no masking anywhere in it); a ragged last tile,
-  // if any, after it. Tile t sits in LDS buffer t & 1; tile t+1 is fetched
-  // from HBM into registers while tile t is multiplied.
+  // Full tiles of the key range in the loop (no masking anywhere in it); the
+  // ragged last tile of the sequence, if it is in the range, after it. Tile t
+  // sits in LDS buffer (t - kt0) & 1; tile t+1 is fetched from HBM into
+  // registers while tile t is multiplied.
+  const int64_t n_tiles = ceil_div(n_kv, ATT_BN);
+  int64_t kt0 = 0, kt1 = n_tiles;
+  if constexpr (SPLIT) key_range(n_tiles, sp.splits, (int)blockIdx.z, kt0, kt1);
   const int64_t n_full = n_kv / ATT_BN;
-  const bool ragged = (n_kv % ATT_BN) != 0;
-  if (n_full > 0)
-    load_full(0);
+  const int64_t fe = kt1 < n_full ? kt1 : n_full;  // end of the range's full tiles
+  const bool tail = (n_kv % ATT_BN) != 0 && kt1 == n_tiles;
+  if (kt0 < fe)
+    load_full(kt0);
   else
-    load_tail(0);
+    load_tail(kt0);
   store_kv(0);
   __syncthreads();
-  for (int64_t t = 0; t < n_full; ++t) {
-    const int cur = (int)(t & 1);
-    const bool fetch = t + 1 < n_full || ragged;
-    if (t + 1 < n_full)
+  for (int64_t t = kt0; t < fe; ++t) {
+    const int cur = (int)((t - kt0) & 1);
+    const bool fetch = t + 1 < fe || tail;
+    if (t + 1 < fe)
       load_full(t + 1);
-    else if (ragged)
+    else if (tail)
       load_tail(t + 1);
     compute(cur, t * ATT_BN, false);
     if (fetch) store_kv(cur ^ 1);
     __syncthreads();
   }
-  if (ragged) compute((int)(n_full & 1), n_full * ATT_BN, true);
+  if (tail) compute((int)((fe - kt0) & 1), n_full * ATT_BN, true);
 
   const float l_all = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_all;
   const int64_t qr = q0 + l32;
+  if constexpr (SPLIT) {  // this range's unnormalised O, its m and l
+    if (qr < n_q) {
+      const int64_t d = (int64_t)gridDim.y * DH;
+      const int64_t prow = (int64_t)blockIdx.z * n_q + qr;
+      float* orow = sp.o_part + prow * d + col0;
+#pragma unroll
+      for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(orow + t * 32 + 8 * qd + 4 * half) =
+              f32x4{acc_o[t][4 * qd], acc_o[t][4 * qd + 1], acc_o[t][4 * qd + 2], acc_o[t][4 * qd + 3]};
+      if (half == 0) {
+        float* ml = sp.ml_part + (prow * gridDim.y + head) * 2;
+        ml[0] = m_run;
+        ml[1] = l_all;
+      }
+    }
+    return;
+  }
+  const float inv = 1.0f / l_all;
   if (qr < n_q) {
     T* orow = o + qr * ldo + col0;
 #pragma unroll
@@ -321,19 +362,26 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
 // and are zeroed when stored, and the tiles after the last reload the last
 // tile into a slot no later phase reads. The compiler then waits for each
 // staged tile by exact count instead of for every outstanding load.
-template <int DH>
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
     const uint16_t* __restrict__ vt, int64_t ldvt, uint16_t* __restrict__ o, int64_t ldo, int64_t n_q,
-    int64_t n_kv, float qk_scale_log2) {
+    int64_t n_kv, float qk_scale_log2, AttSplit sp) {
   using L = AttLayout<uint16_t, DH, 8>;
   constexpr int EPC = L::EPC, KCH = L::KCH, VCH = L::VCH, KRP = L::KRP, VRP = L::VRP;
   constexpr int K_TILE = L::K_TILE, V_TILE = L::V_TILE, K_LD = L::K_LD, V_LD = L::V_LD;
   constexpr int QS = L::QS, OT = L::OT, NTHR = L::NTHR;
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
   const int64_t q_tiles = ceil_div(n_q, L::BM);
-  const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);  // gridDim.x = q_tiles * heads
-  const int64_t head_idx = logical / q_tiles, q_tile = logical % q_tiles;
+  // gridDim.x = heads * splits * q_tiles; each XCD gets a contiguous range of
+  // logical ids, ordered head, key range, query tile, so the workgroups that
+  // stream one head's key range run on one XCD and share its L2
+  const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int splits = SPLIT ? sp.splits : 1;
+  const int64_t head_idx = logical / (splits * q_tiles);
+  const int64_t rem = logical % (splits * q_tiles);
+  const int part = (int)(rem / q_tiles);
+  const int64_t q_tile = rem % q_tiles;
 
   __shared__ __attribute__((aligned(16))) char smem[2 * K_TILE + 2 * V_TILE];
   char* const kring = smem;
@@ -357,6 +405,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t n_tiles = ceil_div(n_kv, ATT_BN);
   const int64_t last_kv0 = (n_tiles - 1) * ATT_BN;
   const bool ragged = (n_kv % ATT_BN) != 0;
+  // this workgroup's key tiles [kt0, kt1); te is the last of them
+  int64_t kt0 = 0, kt1 = n_tiles;
+  if constexpr (SPLIT) key_range(n_tiles, splits, part, kt0, kt1);
+  const int64_t te = kt1 - 1;
   const char* kbase = reinterpret_cast<const char*>(k + col0);
   const char* vbase = reinterpret_cast<const char*>(vt + col0 * ldvt);
   const int64_t k_tile_bytes = (int64_t)ATT_BN * ldk * 2;
@@ -505,21 +557,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: tile 0 in slot 0, tile 1 (or the last tile again) in the staging registers
-  load_k(0);
-  load_v(0);
+  // prologue: tile kt0 in slot 0, tile kt0+1 (or the range's last tile again)
+  // in the staging registers
+  load_k(kt0);
+  load_v(kt0);
   store_k(0);
-  store_v(0, 0);
+  store_v(0, kt0);
   {
-    const int64_t t1 = n_tiles > 1 ? 1 : 0;
+    const int64_t t1 = kt0 + 1 < kt1 ? kt0 + 1 : te;
     load_k(t1);
     load_v(t1);
   }
   __syncthreads();
   if (grp == 1) phase_end();
-  for (int64_t t = 0; t < n_tiles; ++t) {
-    const int cur = (int)(t & 1);
-    const int64_t t2 = t + 2 < n_tiles ? t + 2 : n_tiles - 1;
+  for (int64_t t = kt0; t < kt1; ++t) {
+    const int cur = (int)((t - kt0) & 1);
+    const int64_t t2 = t + 2 < kt1 ? t + 2 : te;
     // M1
     u32x4 kf[QS][2];
     {
@@ -555,10 +608,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // the LDS traffic of this phase (fragment reads, tile store) is issued
     // first and runs under the softmax
     if (ragged && t == n_tiles - 1) mask_last(s);
-    if (t == 0) m_run = tile_max(s);  // tile 0 sets each query's running max exactly
+    if (t == kt0) m_run = tile_max(s);  // the first tile sets each query's running max exactly
     u32x4 pb[4];
     settle(s, pb, exp_tile(s, pb));
-    store_v(cur ^ 1, t + 1 < n_tiles ? t + 1 : n_tiles - 1);
+    store_v(cur ^ 1, t + 1 < kt1 ? t + 1 : te);
     load_v(t2);
     phase_end();
     // C2
@@ -572,12 +625,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (grp == 0) phase_end();
 
   const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float inv = 1.0f / (__uint_as_float(lr[0]) + __uint_as_float(lr[1]));
+  const float l_all = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
   // the output address is formed here from the thread id (passed through an
   // empty asm), not kept in registers across the key loop
   int tid_e = tid;
   asm volatile("" : "+v"(tid_e));
   const int64_t qr = q_tile * L::BM + (tid_e >> 6) * 32 + (tid_e & 31);
+  if constexpr (SPLIT) {  // this range's unnormalised O, its m and l
+    if (qr < n_q) {
+      const int64_t n_heads = gridDim.x / ((int64_t)splits * q_tiles);
+      const int64_t prow = (int64_t)part * n_q + qr;
+      float* orow = sp.o_part + prow * (n_heads * DH) + col0;
+#pragma unroll
+      for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(orow + t * 32 + 8 * qd + 4 * half) =
+              f32x4{acc_o[t][4 * qd], acc_o[t][4 * qd + 1], acc_o[t][4 * qd + 2], acc_o[t][4 * qd + 3]};
+      if (half == 0) {
+        float* ml = sp.ml_part + (prow * n_heads + head_idx) * 2;
+        ml[0] = m_run;
+        ml[1] = l_all;
+      }
+    }
+    return;
+  }
+  const float inv = 1.0f / l_all;
   if (qr < n_q) {
     uint16_t* orow = o + qr * ldo + col0;
 #pragma unroll
@@ -592,44 +665,114 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Merge of the key ranges, one thread per (query, 4 output columns): m =
+// max_p m_p, w_p = exp2((m_p - m) * c), O = (sum_p w_p O_p) / (sum_p w_p l_p),
+// the sums taken in order p = 0, 1, ...; every operation is fixed, so a
+// query's O depends only on its own partials.
+template <typename T>
+__global__ __launch_bounds__(256) void attention_combine_kernel(const float* __restrict__ o_part,
+                                                                const float* __restrict__ ml_part, T* __restrict__ o,
+                                                                int64_t ldo, int64_t n_q, int n_heads, int head_dim,
+                                                                int splits, float qk_scale_log2) {
+  const int64_t d = (int64_t)n_heads * head_dim;
+  const int64_t groups = d / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / groups;
+  if (row >= n_q) return;
+  const int64_t col = (idx % groups) * 4;
+  const int64_t head = col / head_dim;
+  float m = -INFINITY;
+  for (int p = 0; p < splits; ++p) m = fmaxf(m, ml_part[(((int64_t)p * n_q + row) * n_heads + head) * 2]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int p = 0; p < splits; ++p) {
+    const int64_t prow = (int64_t)p * n_q + row;
+    const float* ml = ml_part + (prow * n_heads + head) * 2;
+    const float w = __builtin_amdgcn_exp2f((ml[0] - m) * qk_scale_log2);
+    l = __builtin_fmaf(w, ml[1], l);
+    const f32x4 op = *reinterpret_cast<const f32x4*>(o_part + prow * d + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, op[e], acc[e]);
+  }
+  const float inv = 1.0f / l;
+  T* orow = o + row * ldo + col;
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  } else {
+    *reinterpret_cast<u32x2*>(orow) =
+        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
 template <int DH>
 static hipError_t launch_att_bf16(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
                                   int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int n_heads,
-                                  hipStream_t st) {
+                                  const AttSplit& sp, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  // one-dimensional grid: the kernel derives (head, query tile) from blockIdx.x
-  dim3 grid((unsigned)(ceil_div(n_q, AttLayout<uint16_t, DH, 8>::BM) * n_heads)), block(512);
-  hipLaunchKernelGGL((attention_bf16_kernel<DH>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
+  // one-dimensional grid: the kernel derives (head, key range, query tile) from blockIdx.x
+  dim3 grid((unsigned)(ceil_div(n_q, AttLayout<uint16_t, DH, 8>::BM) * n_heads * sp.splits)), block(512);
+  if (sp.splits == 1) {
+    hipLaunchKernelGGL((attention_bf16_kernel<DH, false>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
+                       static_cast<const uint16_t*>(k), ldk, static_cast<const uint16_t*>(vt), ldvt,
+                       static_cast<uint16_t*>(o), ldo, n_q, n_kv, scale_log2, sp);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attention_bf16_kernel<DH, true>), grid, block, 0, st, static_cast<const uint16_t*>(q), ldq,
                      static_cast<const uint16_t*>(k), ldk, static_cast<const uint16_t*>(vt), ldvt,
-                     static_cast<uint16_t*>(o), ldo, n_q, n_kv, scale_log2);
+                     static_cast<uint16_t*>(o), ldo, n_q, n_kv, scale_log2, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = n_q * (n_heads * DH / 4);
+  hipLaunchKernelGGL((attention_combine_kernel<uint16_t>), dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, st,
+                     sp.o_part, sp.ml_part, static_cast<uint16_t*>(o), ldo, n_q, n_heads, DH, sp.splits, scale_log2);
   return hipGetLastError();
 }
 
 template <typename T, int DH, int NW>
 static hipError_t launch_att_t(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
                                int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int n_heads,
-                               hipStream_t st) {
+                               const AttSplit& sp, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  dim3 grid((unsigned)ceil_div(n_q, AttLayout<T, DH, NW>::BM), (unsigned)n_heads), block(NW * 64);
-  hipLaunchKernelGGL((attention_kernel<T, DH, NW>), grid, block, 0, st, static_cast<const T*>(q), ldq,
+  dim3 grid((unsigned)ceil_div(n_q, AttLayout<T, DH, NW>::BM), (unsigned)n_heads, (unsigned)sp.splits),
+      block(NW * 64);
+  if (sp.splits == 1) {
+    hipLaunchKernelGGL((attention_kernel<T, DH, NW, false>), grid, block, 0, st, static_cast<const T*>(q), ldq,
+                       static_cast<const T*>(k), ldk, static_cast<const T*>(vt), ldvt, static_cast<T*>(o), ldo,
+                       n_q, n_kv, scale_log2, sp);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attention_kernel<T, DH, NW, true>), grid, block, 0, st, static_cast<const T*>(q), ldq,
                      static_cast<const T*>(k), ldk, static_cast<const T*>(vt), ldvt, static_cast<T*>(o), ldo,
-                     n_q, n_kv, scale_log2);
+                     n_q, n_kv, scale_log2, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = n_q * (n_heads * DH / 4);
+  hipLaunchKernelGGL((attention_combine_kernel<T>), dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, st,
+                     sp.o_part, sp.ml_part, static_cast<T*>(o), ldo, n_q, n_heads, DH, sp.splits, scale_log2);
   return hipGetLastError();
+}
+
+int64_t attention_splits_effective(int64_t splits, int64_t n_kv) {
+  const int64_t tiles = ceil_div(n_kv, (int64_t)ATT_BN);
+  return splits < tiles ? splits : tiles;
 }
 
 hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
                             const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q,
-                            int64_t n_kv, int n_heads, int head_dim, hipStream_t st) {
+                            int64_t n_kv, int n_heads, int head_dim, int64_t splits, float* o_part, float* ml_part,
+                            hipStream_t st) {
   if (n_q <= 0) return hipSuccess;
-  if (n_kv <= 0) return hipErrorInvalidValue;
+  if (n_kv <= 0 || splits < 1) return hipErrorInvalidValue;
   // per-thread offsets into a V^T tile are 32-bit: head_dim rows of ldvt elements
   if ((int64_t)head_dim * ldvt * (dtype == F32 ? 4 : 2) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  AttSplit sp{(int)attention_splits_effective(splits, n_kv), o_part, ml_part};
+  if (sp.splits > 1 && (!o_part || !ml_part)) return hipErrorInvalidValue;
   if (dtype == F32) {
-    if (head_dim == 64) return launch_att_t<float, 64, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
-    if (head_dim == 128) return launch_att_t<float, 128, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 64) return launch_att_t<float, 64, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, sp, st);
+    if (head_dim == 128) return launch_att_t<float, 128, 4>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, sp, st);
   } else {
-    if (head_dim == 64) return launch_att_bf16<64>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
-    if (head_dim == 128) return launch_att_bf16<128>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, st);
+    if (head_dim == 64) return launch_att_bf16<64>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, sp, st);
+    if (head_dim == 128) return launch_att_bf16<128>(q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, sp, st);
   }
   return hipErrorInvalidValue;
 }

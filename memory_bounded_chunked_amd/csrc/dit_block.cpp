@@ -34,6 +34,7 @@ struct dit_block {
   dit_block_desc desc;
   dit_block_weights w;
   dit_block_lora lora;  // rank 0 = no adapter
+  int64_t att_splits;   // key ranges per query in attention (1 = none)
 };
 
 // Workspace of dit_block_forward_noalloc: one copy per GPU, loaded with the
@@ -51,9 +52,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t act_bytes(int dtype) { return dtype == DIT_F32 ? 4 : 2; }
 
 struct Plan {
-  int64_t n, ca, cm, fc, s, np;
-  size_t off_k, off_vt, off_stage, off_slab, slab_b, off_lora, total;
+  int64_t n, ca, cm, fc, s, np, splits;
+  size_t off_k, off_vt, off_stage, off_slab, slab_b, off_opart, off_ml, off_lora, total;
 };
+
+// Bytes of the partial results of `splits` (effective) key ranges for n_q queries.
+size_t split_part_bytes(int64_t splits, int64_t n_q, int64_t d, int64_t heads, size_t* ml_off) {
+  if (splits <= 1) {
+    *ml_off = 0;
+    return 0;
+  }
+  const size_t o_bytes = round_up((size_t)splits * n_q * d * 4, kAlign);
+  *ml_off = o_bytes;
+  return o_bytes + round_up((size_t)splits * n_q * heads * 2 * 4, kAlign);
+}
 
 // Adapter ranks of one handle (0 = none).
 struct Ranks {
@@ -89,12 +101,17 @@ int make_plan(const dit_block* h, int64_t n, int64_t attn_chunk, int64_t mlp_chu
   const Ranks r = ranks_of(h);
   const size_t lora_bytes =
       r.any() ? round_up((size_t)4 * std::max(p->ca * r.attn(), p->cm * r.mlp()), kAlign) : 0;
+  p->splits = dit::attention_splits_effective(h->att_splits, n);
+  size_t ml_off = 0;
+  const size_t part_bytes = split_part_bytes(p->splits, p->ca, d, h->desc.n_heads, &ml_off);
   p->off_k = 0;
   p->off_vt = k_bytes;
   p->off_stage = p->off_vt + vt_bytes;
   p->off_slab = p->off_stage + stage_bytes;
   p->slab_b = attn_a;  // offset of the Q slab within the slab region
-  p->off_lora = p->off_slab + std::max(2 * attn_a, mlp_a + mlp_h);
+  p->off_opart = p->off_slab + std::max(2 * attn_a, mlp_a + mlp_h);
+  p->off_ml = p->off_opart + ml_off;
+  p->off_lora = p->off_opart + part_bytes;
   p->total = p->off_lora + lora_bytes;
   return DIT_OK;
 }
@@ -199,6 +216,7 @@ int dit_block_create(const dit_block_desc* desc, const dit_block_weights* w, dit
   h->desc = d;
   h->w = *w;
   std::memset(&h->lora, 0, sizeof(h->lora));
+  h->att_splits = 1;
   *out = h;
   return DIT_OK;
 }
@@ -220,6 +238,12 @@ int dit_block_set_lora(dit_block* h, const dit_block_lora* lora) {
   dit_lora* mine[7] = {&h->lora.q, &h->lora.k, &h->lora.v, &h->lora.o, &h->lora.gate, &h->lora.up, &h->lora.down};
   for (dit_lora* l : mine)
     if (l->rank == 0) *l = dit_lora{nullptr, nullptr, 0, 0.f};
+  return DIT_OK;
+}
+
+int dit_block_set_attention_splits(dit_block* h, int64_t splits) {
+  if (!h || splits < 1 || splits > 64) return DIT_EINVAL;
+  h->att_splits = splits;
   return DIT_OK;
 }
 
@@ -438,7 +462,8 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
                                               rope_rows(rope_cos, s0), rope_rows(rope_sin, s0), ld_rope,
                                               dsc.eps, st));
       DIT_TRY(DIT_K_ATTENTION, launch_attention(dt, slab_b, d, kbuf, d, vtbuf, p.np, slab_a, d, c, n, (int)dsc.n_heads,
-                               (int)dsc.head_dim, st));
+                                                (int)dsc.head_dim, p.splits, reinterpret_cast<float*>(ws + p.off_opart),
+                                                reinterpret_cast<float*>(ws + p.off_ml), st));
       GemmArgs o{};
       o.a = slab_a;
       o.lda = d;
@@ -604,7 +629,46 @@ int dit_attention(int32_t dtype, const void* q, int64_t ldq, const void* k, int6
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return DIT_EINVAL;
   if (n_q == 0) return DIT_OK;
   return hip_status(dit::launch_attention(dtype, q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, (int)n_heads,
-                                          (int)head_dim, static_cast<hipStream_t>(stream)));
+                                          (int)head_dim, 1, nullptr, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int dit_attention_split_workspace(int64_t n_q, int64_t n_kv, int64_t n_heads, int64_t head_dim, int64_t splits,
+                                  size_t* bytes_out) {
+  if (!bytes_out || n_q < 0 || n_kv < 1 || n_heads < 1 || head_dim < 1 || splits < 1 || splits > 64)
+    return DIT_EINVAL;
+  size_t ml_off = 0;
+  *bytes_out = split_part_bytes(dit::attention_splits_effective(splits, n_kv), n_q, n_heads * head_dim, n_heads,
+                                &ml_off);
+  return DIT_OK;
+}
+
+int dit_attention_split(int32_t dtype, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
+                        int64_t ldvt, void* o, int64_t ldo, int64_t n_q, int64_t n_kv, int64_t n_heads,
+                        int64_t head_dim, int64_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (splits < 1 || splits > 64) return DIT_EINVAL;
+  size_t need = 0;
+  if (n_q >= 0 && n_kv >= 1 && n_heads >= 1 &&
+      dit_attention_split_workspace(n_q, n_kv, n_heads, head_dim, splits, &need) != DIT_OK)
+    return DIT_EINVAL;
+  const int64_t s_eff = n_kv >= 1 ? dit::attention_splits_effective(splits, n_kv) : 1;
+  if (s_eff == 1) return dit_attention(dtype, q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, n_heads, head_dim, stream);
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_EINVAL;
+  if (!q || !k || !vt || !o || n_q < 0 || n_heads < 1) return DIT_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return DIT_EINVAL;
+  const int64_t d = n_heads * head_dim;
+  if (ldq < d || ldk < d || ldo < d || ldvt < n_kv) return DIT_EINVAL;
+  if (ldq % 8 || ldk % 8 || ldo % 8 || ldvt % 8) return DIT_EINVAL;
+  if (head_dim * ldvt * (dtype == DIT_F32 ? 4 : 2) >= ((int64_t)1 << 32)) return DIT_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return DIT_EINVAL;
+  if (!workspace || !aligned16(workspace)) return DIT_EINVAL;
+  if (workspace_bytes < need) return DIT_ENOSPC;
+  if (n_q == 0) return DIT_OK;
+  size_t ml_off = 0;
+  split_part_bytes(s_eff, n_q, d, n_heads, &ml_off);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(dit::launch_attention(dtype, q, ldq, k, ldk, vt, ldvt, o, ldo, n_q, n_kv, (int)n_heads,
+                                          (int)head_dim, splits, reinterpret_cast<float*>(ws),
+                                          reinterpret_cast<float*>(ws + ml_off), static_cast<hipStream_t>(stream)));
 }
 
 int dit_linear(int32_t dtype, int32_t epilogue, const void* a, int64_t lda, const void* w, int64_t ldw,

@@ -94,8 +94,15 @@ hipError_t launch_final_layer(int x_f32, const void* x, int64_t ldx, int64_t n, 
 // K3: softmax attention of n_q query rows against n_kv keys for all heads.
 // q [n_q][ldq], k [n_kv][ldk], vt [n_heads*head_dim][ldvt] (V transposed),
 // o [n_q][ldo]; head h owns columns h*head_dim.. of q, k, o and rows of vt.
+// splits > 1: each query's keys in attention_splits_effective(splits, n_kv)
+// contiguous ranges of 64-key tiles, merged by a second kernel; o_part
+// [S][n_q][n_heads*head_dim] and ml_part [S][n_q][n_heads][2] fp32 hold the
+// ranges' partial results (S = the effective split count).
 hipError_t launch_attention(int dtype, const void* q, int64_t ldq, const void* k, int64_t ldk,
                             const void* vt, int64_t ldvt, void* o, int64_t ldo, int64_t n_q,
-                            int64_t n_kv, int n_heads, int head_dim, hipStream_t st);
+                            int64_t n_kv, int n_heads, int head_dim, int64_t splits, float* o_part, float* ml_part,
+                            hipStream_t st);
+// Key ranges actually used for `splits` requested: at most one per 64-key tile.
+int64_t attention_splits_effective(int64_t splits, int64_t n_kv);
 
 }  // namespace dit

@@ -161,6 +161,32 @@ def test_noalloc_forward_rejects_before_any_device_call(lib):
     lib.dit_block_destroy(h)
 
 
+def test_attention_splits_workspace_and_validation(lib):
+    rc, h = _handle(lib)
+    assert rc == 0
+    for bad in (0, -1, 65):
+        assert lib.dit_block_set_attention_splits(h, bad) == B.DIT_EINVAL
+    n, ca, cm, d, heads = 1000, 256, 256, 256, 2
+    _, base = _ws(lib, h, n, ca, cm, 0)
+    assert base == _closed_form(n, d, 512, 2, ca, cm, 0)
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    for splits, eff in ((1, 1), (4, 4), (64, 16)):  # at most one range per 64-key tile (ceil(1000/64) = 16)
+        assert lib.dit_block_set_attention_splits(h, splits) == 0
+        _, ws = _ws(lib, h, n, ca, cm, 0)
+        extra = 0 if eff == 1 else r(eff * ca * d * 4) + r(eff * ca * heads * 2 * 4)
+        assert ws == base + extra, splits
+        out = ctypes.c_size_t()
+        assert lib.dit_attention_split_workspace(ca, n, heads, 128, splits, ctypes.byref(out)) == 0
+        assert out.value == extra
+    lib.dit_block_destroy(h)
+    p = 0x10000
+    f = lib.dit_attention_split
+    assert f(1, p, 256, p, 256, p, 1000, p, 256, 10, 1000, 2, 128, 0, p, 1 << 20, None) == B.DIT_EINVAL
+    assert f(1, p, 256, p, 256, p, 1000, p, 256, 10, 1000, 2, 128, 4, p, 100, None) == B.DIT_ENOSPC
+    assert f(1, p, 256, p, 256, p, 1000, p, 256, 10, 1000, 2, 128, 4, p + 8, 1 << 20, None) == B.DIT_EINVAL
+    assert f(1, p, 256, p, 256, p, 1000, p, 256, 0, 1000, 2, 128, 4, p, 1 << 20, None) == B.DIT_OK
+
+
 def test_step_entry_points_reject_before_launch(lib):
     p = 0x10000
     assert lib.dit_modnorm(1, 1, p, 256, p, p, p, 256, 10, 250, 1e-6, None) == B.DIT_EINVAL

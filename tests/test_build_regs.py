@@ -1,10 +1,7 @@
 """Register allocation of the built library (CPU): no kernel spills VGPRs to
 scratch, except the int8-weight 256x256 GEMM kernels that carry the adapter
 phase (launched only with adapters; it runs after the main loop with all
-accumulators live, and their forms without it do not spill), and
-the bf16 attention kernel with head_dim 128, which spills a few values that
-live only before and after its key loop (plus one reload on the masking
-path of a ragged last key tile), at most 8 VGPRs.
+accumulators live, and their forms without it do not spill).
 A spill inside a hot loop costs far more than it looks (scratch traffic goes
 through L2 and shows up as HBM fetches), so any new spill fails here.
 
@@ -29,7 +26,6 @@ INT8_ADAPTER_SPILLS = {0: 85, 1: 84, 2: 83, 3: 190, 4: 83, 5: 83, 6: 183}
 ALLOWED = {  # kernel: most spilled VGPRs allowed
     **{f"_ZN3dit11gemm_kernelItaLi{epi}ELi256ELi256ELi2ELi4ELb1EEEvNS_8GemmArgsE": n
        for epi, n in INT8_ADAPTER_SPILLS.items()},
-    "_ZN3dit21attention_bf16_kernelILi128EEEvPKtlS2_lS2_lPtlllf": 8,  # outside the key loop
 }
 
 

@@ -185,3 +185,33 @@ def test_block_with_qk_norm_and_rope(key):
         check_bf16_bar(y, y_ref)
     # the transform matters: without it the output differs from the reference
     assert max_abs(to_f64(run_block(shape, inputs, 256, 256)), y_ref) > 1e-3
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+def test_attention_splits_bit_identical_across_chunks(case, splits):
+    # with a key split (fixed per block) the bytes are again identical for every
+    # (attn_chunk_tokens, mlp_chunk_tokens), and the block meets the same bar
+    shape, inputs, x, y_ref = case
+    n = shape.n_tokens
+
+    def run(ca, cm, poison=False):
+        blk, xx, mod = B.block_from_inputs(shape, inputs, "cuda")
+        blk.set_attention_splits(splits)
+        ws = torch.empty(blk.peak_workspace(n, ca, cm), dtype=torch.uint8, device="cuda")
+        if poison:
+            ws.fill_(0xFF)
+        blk.forward(xx, mod, ca, cm, workspace=ws)
+        torch.cuda.synchronize()
+        out = xx.cpu()
+        blk.close()
+        return out
+
+    ref = run(0, n)
+    for ca, cm in ((256, 256), (100, 300), (1, 999), (n, 64)):
+        assert bits(run(ca, cm)) == bits(ref), (ca, cm)
+    assert bits(run(128, 192, poison=True)) == bits(ref)
+    y = to_f64(ref)
+    if shape.dtype == "f32":
+        assert max_abs(y, y_ref) <= 1e-4 and rel_l2(y, y_ref) <= 1e-4
+    else:
+        check_bf16_bar(y, y_ref)

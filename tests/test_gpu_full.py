@@ -27,6 +27,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 SWEEPS = {
     "mid": [(4096, 4096, 0), (0, 16384, 0), (3000, 5000, 0)],
+    # key split of 4 ranges per query (dit_block_set_attention_splits), small slices
+    "large-split4": [(2048, 2048, 0), (8192, 8192, 0), (1000, 3000, 0)],
     "large": [(8192, 8192, 0), (0, 32768, 0), (5000, 3000, 0)],
     "longclip": [(8192, 8192, 3456), (16384, 4096, 3456)],
     "int8": [(a, m, 0) for a in (0, 2048, 8192) for m in (2048, 8192)],
@@ -70,10 +72,12 @@ def _gpu_attention_rows(shape, inputs, rows, x0, mod):
 
 @pytest.mark.parametrize("name", list(SWEEPS))
 def test_full_size_parity_and_bit_identity(name):
-    shape = synth.CONFIGS[name]
+    shape = synth.CONFIGS[name.split("-")[0]]
     n = shape.n_tokens
     inputs = synth.make_inputs(shape, seed=0)
     blk, x0, mod = B.block_from_inputs(shape, inputs, "cuda")
+    if name.endswith("-split4"):
+        blk.set_attention_splits(4)
     digests = []
     y_first = None
     for ca, cm, fc in SWEEPS[name]:

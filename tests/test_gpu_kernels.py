@@ -281,6 +281,49 @@ def test_attention_query_slices_bit_identical_sharp_logits():
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
 
 
+@pytest.mark.parametrize("dtype,heads,dh,n_q,n_kv,splits", [
+    ("bf16", 3, 128, 300, 1000, 4), ("bf16", 2, 128, 129, 64, 4), ("bf16", 2, 64, 257, 333, 3),
+    ("bf16", 2, 128, 70, 200, 7), ("f32", 4, 64, 300, 1000, 4), ("f32", 2, 128, 70, 200, 2), ("f32", 2, 64, 5, 7, 8)])
+def test_attention_split_matches_oracle(dtype, heads, dh, n_q, n_kv, splits):
+    # each query's keys in contiguous ranges of 64-key tiles, attended
+    # separately and merged: the same bars as the unsplit kernel; fewer tiles
+    # than ranges fall back to one range per tile (n_kv = 64: one range)
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs(dtype, n_q, n_kv, heads, dh, n_q * 5 + n_kv + splits)
+    out = torch.empty(n_q, heads * dh, dtype=tdt, device=DEV)
+    B.attention_split(tq, tk, tvt, out, heads, splits, n_kv=n_kv)
+    ref = O.attention(q, k, v, heads)
+    got = to_f64(out)
+    if dtype == "f32":
+        assert max_abs(got, ref) <= 1e-5 * max(1.0, np.abs(ref).max())
+    else:
+        assert rel_l2(got, ref) <= 1e-2
+        assert max_abs(got, ref) <= 2e-2 * max(np.abs(ref).max(), 1e-3)
+        assert rel_l2(got, ref) <= 2 * rel_l2(bf16_round(ref), ref) + 4e-3
+    one = torch.empty_like(out)
+    B.attention_split(tq, tk, tvt, one, heads, 1, n_kv=n_kv)
+    plain = torch.empty_like(out)
+    B.attention(tq, tk, tvt, plain, heads, n_kv=n_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu(), plain.cpu())  # one range is the unsplit kernel
+
+
+@pytest.mark.parametrize("scale", [1.0, 3.0])
+def test_attention_split_query_slices_bit_identical(scale):
+    # with the key cut fixed by n_kv and the range count, a query's bits do not
+    # depend on the other queries of the call (slices at any offset), also
+    # with near one-hot softmax, and the ragged last range holds the ragged tile
+    n_q, n_kv = 300, 1000
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, 2, 128, 9, scale=scale)
+    full = torch.empty(n_q, 256, dtype=tdt, device=DEV)
+    B.attention_split(tq, tk, tvt, full, 2, 4, n_kv=n_kv)
+    assert rel_l2(to_f64(full), O.attention(q, k, v, 2)) <= 1e-2
+    for a, b in ((0, 1), (1, 130), (33, 97), (77, 300), (255, 300)):
+        part = torch.empty(b - a, 256, dtype=tdt, device=DEV)
+        B.attention_split(tq[a:b], tk, tvt, part, 2, 4, n_kv=n_kv)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
+
+
 @pytest.mark.parametrize("dtype,heads,dh,rows", [("bf16", 40, 128, 300), ("bf16", 4, 64, 77), ("f32", 4, 64, 130),
                                                  ("f32", 2, 128, 33)])
 @pytest.mark.parametrize("mode", ["norm", "rope", "both"])
