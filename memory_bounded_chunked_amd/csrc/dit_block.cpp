@@ -338,7 +338,6 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
   const char* wqkv = static_cast<const char*>(h->w.w_qkv);
   const float* s_qkv = w8 ? h->w.s_qkv : nullptr;
   const int64_t dh = dsc.head_dim, ld_rope = dh / 2;
-  const bool qk_k = h->w.k_norm || rope_cos, qk_q = h->w.q_norm || rope_cos;
   auto rope_rows = [&](const float* t, int64_t r0) { return t ? t + r0 * ld_rope : nullptr; };
 
   hipError_t err = hipSuccess;
@@ -406,6 +405,13 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
     g.bscale = s_qkv ? s_qkv + d : nullptr;
     g.out = kbuf + s0 * d * e;
     g.ldo = d;
+    // K's RMSNorm and RoPE in the projection's epilogue
+    g.qk_w = h->w.k_norm;
+    g.rope_cs = rope_rows(rope_cos, s0);
+    g.rope_sn = rope_rows(rope_sin, s0);
+    g.ld_rope = ld_rope;
+    g.qk_head_dim = (int)dh;
+    g.qk_eps = dsc.eps;
     const int64_t ldt_kv = rk.k + rk.v;
     if (lo.k.rank || lo.v.rank) {
       if (lo.k.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.k, slab_a, d, c, d, 0, d, ldt_kv, 0, 0));
@@ -427,14 +433,12 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       g.bscale = s_qkv ? s_qkv + 2 * d : nullptr;
       g.out = vtbuf + s0 * e;
       g.ldo = p.np;
+      g.qk_w = nullptr;  // V is not transformed
+      g.rope_cs = g.rope_sn = nullptr;
       with_lora(g, lo.v, 0, nullptr, 0, ldt_kv, 0);
       if (g.lora_t) g.lora_t = tbuf + rk.k;  // V's t columns follow K's
       DIT_TRY(DIT_K_KV_PROJ, launch_gemm(dt, EPI_STORE_T, g, st));
     }
-    if (qk_k)
-      DIT_TRY(DIT_K_QK, launch_qk_transform(f32, kbuf + s0 * d * e, d, c, (int)d, (int)dh, h->w.k_norm,
-                                            rope_rows(rope_cos, s0), rope_rows(rope_sin, s0), ld_rope, dsc.eps,
-                                            st));
   }
 
   // ---- pass 2: super-slices of S tokens
@@ -454,13 +458,16 @@ int dit_block_forward_rope(dit_block* h, void* x, const float* mod, const float*
       g.bscale = s_qkv;
       g.out = slab_b;
       g.ldo = d;
+      // Q's RMSNorm and RoPE in the projection's epilogue
+      g.qk_w = h->w.q_norm;
+      g.rope_cs = rope_rows(rope_cos, s0);
+      g.rope_sn = rope_rows(rope_sin, s0);
+      g.ld_rope = ld_rope;
+      g.qk_head_dim = (int)dh;
+      g.qk_eps = dsc.eps;
       if (lo.q.rank) DIT_TRY(DIT_K_LORA, lora_in(lo.q, slab_a, d, c, d, 0, d, rk.q, 0, 0));
       with_lora(g, lo.q, 0, nullptr, 0, rk.q, 0);
       DIT_TRY(DIT_K_Q_PROJ, launch_gemm(dt, EPI_STORE, g, st));
-      if (qk_q)
-        DIT_TRY(DIT_K_QK, launch_qk_transform(f32, slab_b, d, c, (int)d, (int)dh, h->w.q_norm,
-                                              rope_rows(rope_cos, s0), rope_rows(rope_sin, s0), ld_rope,
-                                              dsc.eps, st));
       DIT_TRY(DIT_K_ATTENTION, launch_attention(dt, slab_b, d, kbuf, d, vtbuf, p.np, slab_a, d, c, n, (int)dsc.n_heads,
                                                 (int)dsc.head_dim, p.splits, reinterpret_cast<float*>(ws + p.off_opart),
                                                 reinterpret_cast<float*>(ws + p.off_ml), st));

@@ -88,11 +88,37 @@ __device__ __forceinline__ void store_act(T* p, float v) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// Lane data movement inside a row of 16 lanes (DPP), without the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xb1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4e;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i of 8 <-> 7 - i
+constexpr int DPP_MIRROR = 0x140;       // lane i of 16 <-> 15 - i
+
+// Sum over the 32 lanes of each half-wave. Every step adds two values that
+// every lane of the pair holds identically (a + b and b + a are the same
+// float), so all 32 lanes end with the same bits, and the order of the sum
+// is fixed by the lane positions alone.
+__device__ __forceinline__ float half_wave_sum(float t) {
+  t += dpp_f32<DPP_XOR1>(t);
+  t += dpp_f32<DPP_XOR2>(t);
+  t += dpp_f32<DPP_HALF_MIRROR>(t);
+  t += dpp_f32<DPP_MIRROR>(t);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LO: whether the kernel carries the adapter phase. int8-weight kernels come
 // in both forms, because that phase follows their main loop and its
 // registers would otherwise cost every int8 launch (spills after the loop);
 // the others always carry it (it runs before the loop, or in fp32).
-template <typename TA, typename TB, int EPI, int BM, int BN, int WM, int WN, bool LO>
+// QKD: head size of the QK RMSNorm / RoPE epilogue (EPI_STORE and EPI_KV
+// only; 64 or 128), or 0 for the form without it, which launches without
+// those transforms run.
+template <typename TA, typename TB, int EPI, int BM, int BN, int WM, int WN, bool LO, int QKD>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   constexpr int NTHR = WM * WN * 64;
   constexpr bool A_F32 = sizeof(TA) == 4;
@@ -599,6 +625,131 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     }
   };
 
+  // QK RMSNorm and RoPE of the stored columns (Q, and the K columns of the K|V
+  // launch), on the fp32 accumulators before the one rounding to the output
+  // type. A wave's columns are 64 wide (WTN = 64 for every tile shape): one
+  // head of 64, or half a head of 128 whose other half is in wave wn ^ 1. Per
+  // token row and head: t <- t / sqrt(mean(t^2) + eps) * w, then (t[2j],
+  // t[2j+1]) <- (a c - b s, a s + b c) with c, s the row's angle j. The sum of
+  // squares is reduced over the 32 lanes of a half-wave (half_wave_sum) and,
+  // for heads of 128, added to the partner wave's through LDS as (even wave) +
+  // (odd wave); every step is fixed, so a row's result depends only on that
+  // row, whatever tile computes it.
+  auto qk_apply = [&]() {
+    static_assert(WTN == 64, "qk epilogue assumes 64-column wave tiles");
+    constexpr int HD = QKD > 0 ? QKD : 64, HP = HD / 2;  // head size, angles per row
+    const int l32 = lane & 31;
+    if constexpr (B_I8) {  // the per-row scale belongs to the projection, before the norm
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        const float sc = col_scale(tn * BN + wn * WTN + j * 32 + l32);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
+      }
+      scaled = false;
+    }
+    // One 32-row block of every wave at a time. The rows' RoPE angles (cos
+    // then sin) are staged through LDS with coalesced 16-byte loads: for every
+    // block at once when they fit beside the partial sums (256-wide tiles),
+    // else block by block. The partial sums of squares go through LDS to the
+    // partner wave.
+    const bool norm = g.qk_w != nullptr, rope = g.rope_cs != nullptr;
+    constexpr int SROWS = WM * 32;               // rows of one block over the workgroup
+    constexpr int RED = WN * SROWS * 4;          // bytes of the partial sums
+    constexpr int CPR = HP / 4;                  // 16-byte angle chunks per row
+    constexpr bool ALL = (int)sizeof(smem) >= MT * SROWS * HP * 8 + RED;  // stage every block at once
+    constexpr int NB = ALL ? MT : 1;             // blocks per staging
+    float* const ang = reinterpret_cast<float*>(smem);  // [NB][2][SROWS][HP]: cos, then sin
+    float* const red = ang + NB * 2 * SROWS * HP;       // [WN][SROWS]
+    auto stage = [&](int i0) {  // angles of blocks i0 .. i0 + NB - 1
+      constexpr int CHUNKS = NB * SROWS * CPR;   // per table
+      for (int c = tid; c < 2 * CHUNKS; c += NTHR) {
+        const int tab = c >= CHUNKS, cc = c - tab * CHUNKS;
+        const int bi = cc / (SROWS * CPR), sr = (cc / CPR) % SROWS, ch = cc % CPR;
+        int64_t row = m0 + (sr >> 5) * WTM + (i0 + bi) * 32 + (sr & 31);
+        row = row < g.M ? row : g.M - 1;
+        const float* src = (tab ? g.rope_sn : g.rope_cs) + row * g.ld_rope + ch * 4;
+        *reinterpret_cast<f32x4*>(ang + ((bi * 2 + tab) * SROWS + sr) * HP + ch * 4) =
+            *reinterpret_cast<const f32x4*>(src);
+      }
+    };
+    float wv[NTL];
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) wv[j] = norm ? g.qk_w[(wn * WTN + j * 32 + l32) % HD] : 1.f;
+    const int jp0 = ((wn * WTN + l32) % HD) >> 1;  // angle index of this lane's pair in column block 0
+    // rotation of a pair (a, b) = (t[2j], t[2j+1]): the even lane forms
+    // a c - b s, the odd lane b c + a s, i.e. self * c + other * (+-s)
+    const float sgn = (l32 & 1) ? 1.f : -1.f;
+    if (ALL) {
+      __syncthreads();  // the tile buffers are no longer read
+      if (rope) stage(0);
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float ss[16];
+      if (norm) {
+        // the 16 rows' sums side by side, step by step (independent chains)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t = 0.f;
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) t = __builtin_fmaf(acc[i][j][r], acc[i][j][r], t);
+          ss[r] = t;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss[r] += dpp_f32<DPP_XOR1>(ss[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss[r] += dpp_f32<DPP_XOR2>(ss[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss[r] += dpp_f32<DPP_HALF_MIRROR>(ss[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss[r] += dpp_f32<DPP_MIRROR>(ss[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss[r]), __float_as_uint(ss[r]), false, false);
+          ss[r] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+      }
+      const int bi = ALL ? i : 0;  // the block's place in the staged angles
+      if (!ALL || (norm && HD == 128)) {
+        __syncthreads();  // the previous block's angles and sums (or the tile buffers) are no longer read
+        if (!ALL && rope) stage(i);
+        if (norm && HD == 128 && l32 == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[wn * SROWS + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = ss[r];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int br = wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // the row's place in the staged block
+        if (norm) {
+          const float tot = HD == 128 ? red[(wn & ~1) * SROWS + br] + red[(wn | 1) * SROWS + br] : ss[r];
+          const float rr = 1.0f / sqrtf(tot * (1.0f / HD) + g.qk_eps);
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) acc[i][j][r] = acc[i][j][r] * rr * wv[j];
+        }
+      }
+      if (rope) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int br = wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float* ac = ang + (bi * 2) * SROWS * HP + br * HP;
+          const float* as = ac + SROWS * HP;
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) {
+            const int jp = (jp0 + j * 16) % HP;  // column block j is 32 columns, 16 pairs, further on
+            const float self = acc[i][j][r];
+            const float other = dpp_f32<DPP_XOR1>(self);
+            acc[i][j][r] = __builtin_fmaf(other, as[jp] * sgn, self * ac[jp]);
+          }
+        }
+      }
+    }
+  };
+
   // ---- epilogue: lane holds C[8*(r/4) + 4*half + r%4][lane%32] of each 32x32 tile
   if constexpr (EPI == EPI_GATEUP) {
 #pragma unroll
@@ -649,6 +800,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
     };
     if constexpr (EPI == EPI_KV) {
       if (tn * BN < g.split) {  // uniform per workgroup: the split is tile-aligned
+        if constexpr (QKD != 0) qk_apply();
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -683,6 +835,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
         }
       }
   } else {
+    if constexpr (EPI == EPI_STORE && QKD != 0) qk_apply();
     // Per 32x32 block: the 16 operand values this lane needs (x for RESID,
     // the fp32 stage for ACCUM and FINAL) are loaded together before any
     // result is stored, so the block waits for memory once rather than once
@@ -728,21 +881,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   }
 }
 
-template <typename TA, typename TB, int EPI, int BN, int WM, int WN>
-static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
+template <typename TA, typename TB, int EPI, int BN, int WM, int WN, int QKD>
+static hipError_t launch_tile_qk(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 256;
   constexpr int OUT_BN = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   const int64_t tiles = ceil_div(g.M, BM) * ((g.N - g.col0) / OUT_BN);
   if constexpr (sizeof(TB) == 1) {
     if (g.lora_t == nullptr) {
-      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, false>), dim3((unsigned)tiles),
+      hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, false, QKD>), dim3((unsigned)tiles),
                          dim3(WM * WN * 64), 0, st, g);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, true>), dim3((unsigned)tiles), dim3(WM * WN * 64),
-                     0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<TA, TB, EPI, BM, BN, WM, WN, true, QKD>), dim3((unsigned)tiles),
+                     dim3(WM * WN * 64), 0, st, g);
   return hipGetLastError();
+}
+
+template <typename TA, typename TB, int EPI, int BN, int WM, int WN>
+static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_KV) {
+    if (g.qk_w || g.rope_cs) {
+      if (g.qk_head_dim == 64) return launch_tile_qk<TA, TB, EPI, BN, WM, WN, 64>(g, st);
+      if (g.qk_head_dim == 128) return launch_tile_qk<TA, TB, EPI, BN, WM, WN, 128>(g, st);
+      return hipErrorInvalidValue;
+    }
+  }
+  return launch_tile_qk<TA, TB, EPI, BN, WM, WN, 0>(g, st);
 }
 
 // Compute units of the current device (cached per device; concurrent callers

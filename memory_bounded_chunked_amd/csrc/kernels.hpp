@@ -56,6 +56,16 @@ struct GemmArgs {
   const void* lora_b[2];
   int64_t lora_r[2];
   int64_t lora_toff[2];
+  // QK RMSNorm (qk_w: fp32 [qk_head_dim], or null) and RoPE (rope_cs /
+  // rope_sn: fp32 [M][ld_rope] angles of this launch's rows, or null) of the
+  // stored columns, per head of qk_head_dim (64 or 128) columns, before the
+  // output is rounded: EPI_STORE, and the first `split` columns of EPI_KV.
+  const float* qk_w;
+  const float* rope_cs;
+  const float* rope_sn;
+  int64_t ld_rope;
+  int qk_head_dim;
+  float qk_eps;
   // Set by launch_gemm only: a launch covers output columns [col0, N).
   int64_t col0;
 };

@@ -1,7 +1,9 @@
 """Register allocation of the built library (CPU): no kernel spills VGPRs to
-scratch, except the int8-weight 256x256 GEMM kernels that carry the adapter
-phase (launched only with adapters; it runs after the main loop with all
-accumulators live, and their forms without it do not spill).
+scratch, except the 256x256 GEMM kernels whose epilogue carries extra work
+with every accumulator live, which spill only after their main loop: the
+int8-weight kernels with the adapter phase (launched only with adapters) and
+the int8 Q and K|V kernels that carry both that phase and the QK RMSNorm /
+RoPE epilogue. Their forms without that work do not spill.
 A spill inside a hot loop costs far more than it looks (scratch traffic goes
 through L2 and shows up as HBM fetches), so any new spill fails here.
 
@@ -23,9 +25,15 @@ LLVM = "/opt/rocm/llvm/bin"
 # register-heavy ones are the SwiGLU and the K|V epilogues). A change in the
 # kernel that spills more fails here and has to be looked at.
 INT8_ADAPTER_SPILLS = {0: 85, 1: 84, 2: 83, 3: 190, 4: 83, 5: 83, 6: 183}
+# (types, epilogue, adapter form, head size): spills of the 256x256 kernels
+# with the QK epilogue; types: ff = fp32, tt = bf16, ta = bf16 activations
+# with int8 weights
+QK_SPILLS = {("ta", 0, 1, 128): 84, ("ta", 0, 1, 64): 81, ("ta", 6, 1, 128): 167, ("ta", 6, 1, 64): 165}
 ALLOWED = {  # kernel: most spilled VGPRs allowed
-    **{f"_ZN3dit11gemm_kernelItaLi{epi}ELi256ELi256ELi2ELi4ELb1EEEvNS_8GemmArgsE": n
+    **{f"_ZN3dit11gemm_kernelItaLi{epi}ELi256ELi256ELi2ELi4ELb1ELi0EEEvNS_8GemmArgsE": n
        for epi, n in INT8_ADAPTER_SPILLS.items()},
+    **{f"_ZN3dit11gemm_kernelI{t}Li{epi}ELi256ELi256ELi2ELi4ELb{lo}ELi{hd}EEEvNS_8GemmArgsE": n
+       for (t, epi, lo, hd), n in QK_SPILLS.items()},
 }
 
 
@@ -64,7 +72,11 @@ def test_no_vgpr_spills(tmp_path):
     assert any("attention_bf16_kernel" in k for k in kernels)
     assert any("lora_t_kernel" in k for k in kernels)
     spilling = {k: v for k, v in kernels.items() if v > ALLOWED.get(k, 0)}
-    # every int8 kernel also exists without the adapter phase, and that form does not spill
-    assert all(k.replace("ELb1E", "ELb0E") in kernels and kernels[k.replace("ELb1E", "ELb0E")] == 0
-               for k in kernels if "gemm_kernelIta" in k)
+    # every GEMM kernel also exists without the extra epilogue work (int8:
+    # neither the adapter phase nor the QK epilogue; others: no QK epilogue),
+    # and that form does not spill
+    def plain(k):
+        return re.sub(r"ELb[01]ELi(0|64|128)EEEvNS_8GemmArgsE$",
+                      ("ELb0" if "gemm_kernelIta" in k else "ELb1") + "ELi0EEEvNS_8GemmArgsE", k)
+    assert all(plain(k) in kernels and kernels[plain(k)] == 0 for k in kernels if "gemm_kernelI" in k)
     assert not spilling, spilling
