@@ -53,7 +53,9 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
   tn = within / rows;
 }
 
-// 16 int8 -> 16 bf16 (exact).
+// 16 int8 -> 16 bf16 (exact): each byte converts to fp32 exactly and every
+// |q| <= 127 is a bf16 value, so the rounding conversion of each pair
+// (v_cvt_pk_bf16_f32) is exact too.
 __device__ __forceinline__ void i8x16_to_bf16(const u32x4& q, u32x4& lo, u32x4& hi) {
   uint32_t w[8];
 #pragma unroll
@@ -63,9 +65,8 @@ __device__ __forceinline__ void i8x16_to_bf16(const u32x4& q, u32x4& lo, u32x4& 
     const float f1 = (float)(int8_t)((v >> 8) & 0xff);
     const float f2 = (float)(int8_t)((v >> 16) & 0xff);
     const float f3 = (float)(int8_t)(v >> 24);
-    // exact: every |q| <= 127 is representable in bf16, so truncation is exact
-    w[2 * j] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-    w[2 * j + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+    w[2 * j] = pack_bf16x2(f0, f1);
+    w[2 * j + 1] = pack_bf16x2(f2, f3);
   }
   lo = u32x4{w[0], w[1], w[2], w[3]};
   hi = u32x4{w[4], w[5], w[6], w[7]};
@@ -554,9 +555,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   // both groups (group 1 takes one more before the loop, group 0 one more
   // after it). Each accumulator still takes k-steps 0, 1, 2, 3 of each tile in
   // order, as in the one-group schedule.
-  // (int8 weights keep the one-group schedule: their widening to bf16 on the
-  // way into LDS made the two-group one 3-8% slower)
-  constexpr bool PP = !A_F32 && !B_I8 && WM * WN == 8;
+  // With int8 weights the B stores of M2 carry the widening to bf16 (one
+  // conversion per weight, one packing conversion per pair).
+  constexpr bool PP = !A_F32 && WM * WN == 8;
   int kt = 0;
   if constexpr (PP) {
     const int grp = wave >> 2;
