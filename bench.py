@@ -308,6 +308,75 @@ def bench_final_layer(args) -> int:
     return 0
 
 
+def library_reference(config: str) -> int:
+    """The platform libraries on the same box and the same shapes as this
+    library's kernels: torch's F.linear (hipBLASLt) on the block's projection
+    shapes and torch's flash SDPA on one attention launch, each timed beside
+    the kernel of this library that does the same product (bf16 weights, the
+    plain-store epilogue; attention with n_kv keys). A context measurement;
+    nothing here is on the block's path. One JSON line."""
+    import torch
+    import torch.nn.functional as F
+
+    from memory_bounded_chunked_amd import block as B
+    from memory_bounded_chunked_amd import synth
+
+    shape = synth.CONFIGS[config]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    d, ffn, heads, dh = shape.d, shape.ffn, shape.n_heads, shape.head_dim
+    ca, cm, n = shape.attn_chunk or shape.n_tokens, shape.mlp_chunk or shape.n_tokens, shape.n_tokens
+
+    def timeit(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    for name, m, k, nn in (("q", ca, d, d), ("kv", ca, d, 2 * d), ("gate_up", cm, d, 2 * ffn), ("down", cm, ffn, d)):
+        a = torch.randn(m, k, device=dev, generator=g).bfloat16()
+        w = (torch.randn(nn, k, device=dev, generator=g) * k ** -0.5).bfloat16()
+        o = torch.empty(m, nn, device=dev, dtype=torch.bfloat16)
+        flops = 2.0 * m * k * nn
+        t_lib = timeit(lambda: B.linear("bf16", "store", a, w, o, nn))
+        t_ref = timeit(lambda: F.linear(a, w))
+        out[name] = {"shape": [m, k, nn], "this_ms": round(t_lib, 4), "this_tflops": round(flops / t_lib / 1e9, 1),
+                     "hipblaslt_ms": round(t_ref, 4), "hipblaslt_tflops": round(flops / t_ref / 1e9, 1)}
+        log(f"[reference] {name}: this {t_lib:.3f} ms, hipBLASLt {t_ref:.3f} ms")
+        del a, w, o
+    q = torch.randn(ca, d, device=dev, generator=g).bfloat16()
+    k = torch.randn(n, d, device=dev, generator=g).bfloat16()
+    vt = torch.randn(d, n, device=dev, generator=g).bfloat16()
+    o = torch.empty(ca, d, device=dev, dtype=torch.bfloat16)
+    flops = 4.0 * ca * n * d
+    t_lib = timeit(lambda: B.attention(q, k, vt, o, heads), reps=5)
+    att = {"shape": [ca, n, heads, dh], "this_ms": round(t_lib, 4), "this_tflops": round(flops / t_lib / 1e9, 1)}
+    # torch's layout: (batch, heads, tokens, dh), contiguous
+    qs = q.view(ca, heads, dh).transpose(0, 1).contiguous().unsqueeze(0)
+    ks = k.view(n, heads, dh).transpose(0, 1).contiguous().unsqueeze(0)
+    vs = vt.view(heads, dh, n).transpose(1, 2).contiguous().unsqueeze(0)
+    del q, k, vt, o
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:  # the named backend only: no fallback to the unfused product
+            with sdpa_kernel([be]):
+                t_ref = timeit(lambda: F.scaled_dot_product_attention(qs, ks, vs), reps=5)
+            att[f"sdpa_{be.name.lower()}_ms"] = round(t_ref, 4)
+            att[f"sdpa_{be.name.lower()}_tflops"] = round(flops / t_ref / 1e9, 1)
+            log(f"[reference] attention: this {t_lib:.3f} ms, SDPA {be.name} {t_ref:.3f} ms")
+        except RuntimeError as ex:
+            att[f"sdpa_{be.name.lower()}"] = f"unavailable: {str(ex)[:80]}"
+    out["attention"] = att
+    print(json.dumps({"reference": {"workload": shape.name, "device": torch.cuda.get_device_name(0), **out}}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +397,9 @@ def main() -> int:
                     help="block forward (default) or the output head after the last block")
     ap.add_argument("--probe", choices=tuple(TRAFFIC), default=None,
                     help="one launch of a kernel plus the calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--reference", action="store_true",
+                    help="time torch's F.linear (hipBLASLt) and flash SDPA beside this library's kernels on the "
+                         "configuration's shapes (context, not the block)")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the traffic record of KERNEL from two counter_collection.csv files")
     args = ap.parse_args()
@@ -339,6 +411,8 @@ def main() -> int:
         return 2
     if args.probe:
         return traffic_probe(args.probe)
+    if args.reference:
+        return library_reference(args.config)
     if args.op == "final_layer":
         return bench_final_layer(args)
 
