@@ -377,6 +377,62 @@ def library_reference(config: str) -> int:
     return 0
 
 
+def copy_roofline(config: str) -> int:
+    """The HBM-bound norm kernels against a plain copy of the same bytes, each
+    launch timed alone from a cold cache (a 1 GiB buffer is rewritten before
+    every launch, more than the last-level cache holds): norm1 (bf16 in, bf16
+    out) against torch's bf16 copy, norm2 (fp32 in, bf16 out) against torch's
+    fp32 -> bf16 copy, at one slab of the configuration and at 65536 rows. The
+    copy is the streaming rate this machine reaches with the same bytes. One JSON
+    line; medians of 7 launches."""
+    import statistics
+
+    import torch
+
+    from memory_bounded_chunked_amd import block as B
+    from memory_bounded_chunked_amd import synth
+
+    shape = synth.CONFIGS[config]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+
+    def cold(fn, reps=7):
+        ts = []
+        for _ in range(reps):
+            flush.add_(1.0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    out = []
+    d = shape.d
+    for rows in sorted({shape.mlp_chunk or shape.n_tokens, 65536}):
+        x = torch.randn(rows, d, device=dev, generator=g).bfloat16()
+        xf = torch.randn(rows, d, device=dev, generator=g)
+        y = torch.empty(rows, d, device=dev, dtype=torch.bfloat16)
+        sh = torch.randn(d, device=dev, generator=g) * 0.1
+        sc = torch.randn(d, device=dev, generator=g) * 0.1
+        b1, b2 = rows * d * 4, rows * d * 6
+        t = {"copy_bf16": cold(lambda: y.copy_(x)), "norm1": cold(lambda: B.modnorm(x, sh, sc, y)),
+             "copy_f32_bf16": cold(lambda: y.copy_(xf)), "norm2": cold(lambda: B.modnorm(xf, sh, sc, y))}
+        rec = {"rows": rows, "d": d}
+        for k, ms in t.items():
+            nb = b1 if k in ("copy_bf16", "norm1") else b2
+            rec[k] = {"us": round(ms * 1e3, 1), "tb_s": round(nb / (ms * 1e-3) / 1e12, 2)}
+        out.append(rec)
+        log(f"[copy] {rows} rows: " + ", ".join(f"{k} {v['us']} us {v['tb_s']} TB/s" for k, v in rec.items()
+                                               if isinstance(v, dict)))
+        del x, xf, y
+    print(json.dumps({"copy_roofline": {"workload": shape.name, "cold_cache": True, "sizes": out}}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +456,8 @@ def main() -> int:
     ap.add_argument("--reference", action="store_true",
                     help="time torch's F.linear (hipBLASLt) and flash SDPA beside this library's kernels on the "
                          "configuration's shapes (context, not the block)")
+    ap.add_argument("--copy-roofline", action="store_true",
+                    help="the norm kernels against a plain copy of the same bytes, each from a cold cache")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the traffic record of KERNEL from two counter_collection.csv files")
     args = ap.parse_args()
@@ -413,6 +471,8 @@ def main() -> int:
         return traffic_probe(args.probe)
     if args.reference:
         return library_reference(args.config)
+    if args.copy_roofline:
+        return copy_roofline(args.config)
     if args.op == "final_layer":
         return bench_final_layer(args)
 
