@@ -329,6 +329,15 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
   }
 }
 
+// Largest tile sum of P before a query's running max moves (2^64). Every P
+// element then stays below 2^64, the row sum below 2^64 per 64-key tile
+// (2^80 at 2^16 tiles, a million keys) and |O| below that times max|V|, so
+// fp32 (to 2^128) and bf16 P (same exponent range) hold them with room for
+// |V| up to 2^40. A high bar keeps moves rare when logits are large (weights
+// of the int8 block give logits of tens to hundreds), where every move costs
+// a rescale of O and a second exponentiation of the tile.
+constexpr float ATT_MOVE_SUM = 18446744073709551616.0f;
+
 // bf16 variant (8 waves) with a two-group schedule. Waves w and w+4 share a
 // SIMD, so waves 0-3 and 4-7 form two groups with one wave per SIMD each;
 // group 1 runs one phase behind group 0. A key tile is four phases, each
@@ -348,13 +357,14 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
 // Softmax: fp32, exp2 with log2(e)/sqrt(dh) folded into one multiply-add.
 // Tile 0 sets each query's running max exactly. Later tiles are
 // exponentiated against the max in use, and only a query whose tile sum
-// leaves [0, 2^16] moves to its new max (its O and row sum rescaled, the
-// tile's P formed again); otherwise P may reach 2^8 per element, which fp32
-// and bf16 hold without loss of relative precision. The decision uses only
-// the query's own scores, so O does not depend on which queries share a
-// wavefront. P is rounded to bf16 and the row sum is accumulated from the
-// rounded values (v_dot2_f32_bf16 against 1.0), the ones that enter the PV
-// product; O is divided by the row sum at the end.
+// leaves [0, ATT_MOVE_SUM] moves to its new max (its O and row sum
+// rescaled, the tile's P formed again); otherwise P may reach ATT_MOVE_SUM
+// per element, which fp32 and bf16 hold without loss of relative precision
+// (see ATT_MOVE_SUM for the range). The decision uses only the query's own
+// scores, so O does not depend on which queries share a wavefront. P is
+// rounded to bf16 and the row sum is accumulated from the rounded values
+// (v_dot2_f32_bf16 against 1.0), the ones that enter the PV product; O is
+// divided by the row sum at the end.
 //
 // Loads carry no branch: key rows past n_kv re-read the last key row (their
 // scores are masked to -inf), V^T chunks past n_kv re-read the last valid
@@ -525,7 +535,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto settle = [&](f32x16 (&s)[2], u32x4 (&pb)[4], float ls) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
-    const bool move = !(__uint_as_float(r[0]) + __uint_as_float(r[1]) <= 65536.0f);
+    const bool move = !(__uint_as_float(r[0]) + __uint_as_float(r[1]) <= ATT_MOVE_SUM);
     if (__any(move)) {
       const float mx = tile_max(s);
       const float m_new = move ? fmaxf(m_run, mx) : m_run;

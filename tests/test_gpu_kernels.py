@@ -195,10 +195,13 @@ def test_linear_gateup(dtype):
     assert torch.equal(sub.cpu(), out[:, 64:].cpu())
 
 
-def _attn_inputs(dtype, n_q, n_kv, heads, dh, seed, scale=1.0):
+def _attn_inputs(dtype, n_q, n_kv, heads, dh, seed, scale=1.0, key_growth=0.0):
+    # key_growth: keys of 64-key tile t scaled by 1 + key_growth * t, so later
+    # tiles hold ever larger logits and running maxima keep moving
     rng = _rng(seed)
     d = heads * dh
     q, k, v = (rng.standard_normal((n, d)) * scale for n in (n_q, n_kv, n_kv))
+    k = k * (1.0 + key_growth * (np.arange(n_kv) // 64))[:, None]
     ld_vt = (n_kv + 63) // 64 * 64
     if dtype == "f32":
         q, k, v = (t.astype(np.float32).astype(np.float64) for t in (q, k, v))
@@ -232,7 +235,8 @@ def test_attention(dtype, heads, dh, n_q, n_kv):
 
 
 def test_attention_sharp_logits():
-    # large logits (near one-hot softmax) exercise the running max and rescaling
+    # large logits (near one-hot softmax); the running max stays where the
+    # first tile put it (moves: test_attention_moving_maxima)
     q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", 200, 700, 2, 128, 5, scale=3.0)
     out = torch.empty(200, 256, dtype=tdt, device=DEV)
     B.attention(tq, tk, tvt, out, 2, n_kv=700)
@@ -268,8 +272,8 @@ def test_attention_every_tile_count_with_poisoned_padding(dh):
 
 
 def test_attention_query_slices_bit_identical_sharp_logits():
-    # near one-hot softmax moves the running max many times; each query must
-    # take those decisions from its own scores only, whatever slice holds it
+    # near one-hot softmax, sliced at offsets that are not multiples of 32
+    # queries (slices with moving maxima: test_attention_moving_maxima)
     n_q, n_kv = 300, 1000
     q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, 2, 128, 5, scale=3.0)
     full = torch.empty(n_q, 256, dtype=tdt, device=DEV)
@@ -277,6 +281,48 @@ def test_attention_query_slices_bit_identical_sharp_logits():
     for a, b in ((0, 1), (1, 130), (33, 97), (77, 300), (255, 300)):
         part = torch.empty(b - a, 256, dtype=tdt, device=DEV)
         B.attention(tq[a:b], tk, tvt, part, 2, n_kv=n_kv)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
+
+
+def _moves_after_first_tile(q, k, heads, dh, bar_log2=64.0):
+    """Per (query, head): how many times the kernel's rule moves the running
+    max after the first 64-key tile (fp64 emulation of the rule: tile 0 sets
+    the max; a later tile whose sum of exp2((s - m) c) exceeds 2^bar_log2
+    moves it to that tile's max). Used to check that inputs exercise moves."""
+    c = np.log2(np.e) / np.sqrt(dh)
+    n_kv = k.shape[0]
+    moves = np.zeros((q.shape[0], heads), dtype=np.int64)
+    for h in range(heads):
+        s = q[:, h * dh:(h + 1) * dh] @ k[:, h * dh:(h + 1) * dh].T
+        m = s[:, :64].max(axis=1)
+        for t0 in range(64, n_kv, 64):
+            st = s[:, t0:t0 + 64]
+            tmax = st.max(axis=1)
+            lsum = np.log2(np.exp2((st - tmax[:, None]) * c).sum(axis=1)) + (tmax - m) * c
+            mv = lsum > bar_log2
+            moves[mv, h] += 1
+            m = np.where(mv, np.maximum(m, tmax), m)
+    return moves
+
+
+def test_attention_moving_maxima():
+    # keys whose tiles grow in scale: each query's running max moves several
+    # times after tile 0, at tiles that differ between queries of one
+    # wavefront; the result must meet the bar and be the same bits in any
+    # query slice (slices not multiples of 32 queries, single rows)
+    n_q, n_kv, heads, dh = 300, 1000, 2, 128
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, heads, dh, 11, scale=3.0, key_growth=0.5)
+    moves = _moves_after_first_tile(q, k, heads, dh)
+    assert (moves > 0).mean() > 0.9 and moves.max() >= 2, np.bincount(moves.ravel())
+    assert len(np.unique(moves[:32].ravel())) > 1  # queries of one wavefront move differently
+    full = torch.empty(n_q, heads * dh, dtype=tdt, device=DEV)
+    B.attention(tq, tk, tvt, full, heads, n_kv=n_kv)
+    ref = O.attention(q, k, v, heads)
+    assert rel_l2(to_f64(full), ref) <= 1e-2
+    for a, b in ((0, 1), (1, 130), (33, 97), (77, 300), (255, 300), (296, 297)):
+        part = torch.empty(b - a, heads * dh, dtype=tdt, device=DEV)
+        B.attention(tq[a:b], tk, tvt, part, heads, n_kv=n_kv)
         torch.cuda.synchronize()
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
 
@@ -352,14 +398,14 @@ def test_qk_transform(dtype, heads, dh, rows, mode):
 
 def test_attention_query_independent_of_wave_mates_with_moving_maxima():
     # Q, K and V^T of an int8-weight block (d = 4096, 32 heads x 128, 1024
-    # tokens) through the step kernels: per-head logits reach tens of units,
-    # so running maxima move in later key tiles for some queries of a
-    # wavefront and not for others, and a wave whose query moves exponentiates
-    # its tile again. A query's O must not depend on the queries that share its
-    # wavefront: slices starting at offsets that are not multiples of 32, and
-    # single rows, must give the bits of the full launch (with the second
-    # exponentiation compiled differently from the first, query 296 of head 23
-    # did not).
+    # tokens) through the step kernels: per-head logits reach tens of units.
+    # A query's O must not depend on the queries that share its wavefront:
+    # slices starting at offsets that are not multiples of 32, and single
+    # rows, must give the bits of the full launch. (Under the earlier move bar
+    # of 2^16 these logits moved running maxima in later tiles, and with the
+    # second exponentiation compiled differently from the first, query 296 of
+    # head 23 did not; under the 2^64 bar moves are exercised by
+    # test_attention_moving_maxima.)
     shape = synth.BlockShape("att-mates", 4096, 32, 128, 2048, 1024, "w8_bf16")
     inp = synth.make_inputs(shape, 0)
     t = {k: B.tensor_from_stored(v, DEV) for k, v in inp.items()}
