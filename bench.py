@@ -433,6 +433,71 @@ def copy_roofline(config: str) -> int:
     return 0
 
 
+def secondary_configs(steps: int) -> dict:
+    """Short timing of the other block configurations at their own chunk
+    settings (one warm-up, `steps` timed forwards each, HIP events on the
+    library's stream), so that one default run records them beside the large
+    block: the mid block (also with two key ranges per query, its measured
+    best), the long clip with FFN feature slices and the int8-weight block."""
+    import torch
+
+    from memory_bounded_chunked_amd import block as B
+    from memory_bounded_chunked_amd import synth
+    dev = "cuda:0"
+    out = {}
+    for name, splits in (("mid", 1), ("mid", 2), ("longclip", 1), ("int8", 1)):
+        shape = synth.CONFIGS[name]
+        t0 = time.perf_counter()
+        inputs = synth.make_inputs(shape, seed=0)
+        blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
+        del inputs
+        if splits != 1:
+            blk.set_attention_splits(splits)
+        ca, cm, fc = shape.attn_chunk, shape.mlp_chunk, shape.ffn_chunk
+        ws_bytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        x = x0.clone()
+        stream = torch.cuda.current_stream()
+
+        def step():
+            x.copy_(x0)
+            blk.forward(x, mod, ca, cm, fc, workspace=ws, stream=stream)
+
+        step()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        # the restoring copy of x is inside each step; time it alone to report the forward
+        ev0.record(stream)
+        for _ in range(steps):
+            x.copy_(x0)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = ev0.elapsed_time(ev1) / steps
+        tflops = shape.flops / (ms / 1e3) / 1e12
+        key = name if splits == 1 else f"{name}_splits{splits}"
+        out[key] = {
+            "n_tokens": shape.n_tokens, "d": shape.d, "dtype": shape.dtype,
+            "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
+            **({"attention_splits": splits} if splits != 1 else {}),
+            "steps": steps, "ms_per_step": round(ms, 3), "copy_ms_per_step": round(copy_ms, 3),
+            "tokens_per_s": round(shape.n_tokens / (ms / 1e3), 1),
+            "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "peak_workspace_bytes": ws_bytes,
+        }
+        log(f"[bench] secondary {key}: {ms:.3f} ms/step ({tflops:.0f} TFLOP/s) incl. setup "
+            f"{time.perf_counter() - t0:.1f}s")
+        blk.close()
+        del x, x0, ws, mod
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +525,9 @@ def main() -> int:
                     help="the norm kernels against a plain copy of the same bytes, each from a cold cache")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the traffic record of KERNEL from two counter_collection.csv files")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the short timing of the other configurations that the default run adds")
+    ap.add_argument("--secondary-steps", type=int, default=3)
     args = ap.parse_args()
     if args.record_traffic:
         return record_traffic(*args.record_traffic)
@@ -609,6 +677,10 @@ def main() -> int:
     blk.close()
     del x, x0, ws
     torch.cuda.empty_cache()
+    default_run = (args.config == "large" and not (args.qk or args.lora) and args.attn_splits == 1
+                   and args.attn_chunk is None and args.mlp_chunk is None and args.ffn_chunk is None)
+    if default_run and not args.no_secondary:
+        result["secondary"] = secondary_configs(args.secondary_steps)
     if not args.no_cpu_baseline and not args.lora:
         log("[bench] cpu_baseline: fp64 oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_rows)
