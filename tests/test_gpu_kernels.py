@@ -327,6 +327,28 @@ def test_attention_moving_maxima():
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
 
 
+def test_attention_overflowing_logits():
+    # one key tile whose logits exceed the first tile's max by hundreds of
+    # log2 units: its exponentials overflow fp32 (inf), which must move the
+    # running max (the sum test is false for inf), not reach O; and a first
+    # tile far above the rest, whose later exponentials underflow to zero
+    n_q, n_kv, heads, dh = 96, 640, 2, 128
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, heads, dh, 17, scale=3.0)
+    for hot in (5, 0):
+        k2 = k.copy()
+        k2[64 * hot:64 * hot + 64] *= 20.0
+        k2 = bf16_round(k2)
+        moves = _moves_after_first_tile(q, k2, heads, dh)
+        if hot:
+            assert (moves > 0).all()
+        out = torch.empty(n_q, heads * dh, dtype=tdt, device=DEV)
+        B.attention(tq, _bf16(k2), tvt, out, heads, n_kv=n_kv)
+        ref = O.attention(q, k2, v, heads)
+        got = to_f64(out)
+        assert np.isfinite(got).all(), hot
+        assert rel_l2(got, ref) <= 1e-2, hot
+
+
 @pytest.mark.parametrize("dtype,heads,dh,n_q,n_kv,splits", [
     ("bf16", 3, 128, 300, 1000, 4), ("bf16", 2, 128, 129, 64, 4), ("bf16", 2, 64, 257, 333, 3),
     ("bf16", 2, 128, 70, 200, 7), ("f32", 4, 64, 300, 1000, 4), ("f32", 2, 128, 70, 200, 2), ("f32", 2, 64, 5, 7, 8)])
