@@ -446,11 +446,25 @@ def secondary_configs(steps: int) -> dict:
     dev = "cuda:0"
     out = {}
     for name, splits in (("mid", 1), ("mid", 2), ("longclip", 1), ("int8", 1)):
-        shape = synth.CONFIGS[name]
-        t0 = time.perf_counter()
-        inputs = synth.make_inputs(shape, seed=0)
-        blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
-        del inputs
+        key = name if splits == 1 else f"{name}_splits{splits}"
+        try:
+            out[key] = _time_secondary(B, synth, dev, name, splits, steps)
+        except Exception as e:  # reported in the record; the headline line still prints
+            out[key] = {"error": f"{type(e).__name__}: {e}"}
+            log(f"[bench] secondary {key} failed: {e}")
+        torch.cuda.empty_cache()
+    return out
+
+
+def _time_secondary(B, synth, dev, name, splits, steps) -> dict:
+    """One configuration of secondary_configs: its record."""
+    import torch
+    shape = synth.CONFIGS[name]
+    t0 = time.perf_counter()
+    inputs = synth.make_inputs(shape, seed=0)
+    blk, x0, mod = B.block_from_inputs(shape, inputs, dev)
+    del inputs
+    try:
         if splits != 1:
             blk.set_attention_splits(splits)
         ca, cm, fc = shape.attn_chunk, shape.mlp_chunk, shape.ffn_chunk
@@ -463,39 +477,33 @@ def secondary_configs(steps: int) -> dict:
             x.copy_(x0)
             blk.forward(x, mod, ca, cm, fc, workspace=ws, stream=stream)
 
+        def timed(fn) -> float:
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(steps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / steps
+
         step()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(steps):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / steps
-        # the restoring copy of x is inside each step; time it alone to report the forward
-        ev0.record(stream)
-        for _ in range(steps):
-            x.copy_(x0)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        copy_ms = ev0.elapsed_time(ev1) / steps
-        tflops = shape.flops / (ms / 1e3) / 1e12
-        key = name if splits == 1 else f"{name}_splits{splits}"
-        out[key] = {
-            "n_tokens": shape.n_tokens, "d": shape.d, "dtype": shape.dtype,
-            "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
-            **({"attention_splits": splits} if splits != 1 else {}),
-            "steps": steps, "ms_per_step": round(ms, 3), "copy_ms_per_step": round(copy_ms, 3),
-            "tokens_per_s": round(shape.n_tokens / (ms / 1e3), 1),
-            "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "peak_workspace_bytes": ws_bytes,
-        }
-        log(f"[bench] secondary {key}: {ms:.3f} ms/step ({tflops:.0f} TFLOP/s) incl. setup "
-            f"{time.perf_counter() - t0:.1f}s")
+        ms = timed(step)
+        copy_ms = timed(lambda: x.copy_(x0))  # the restoring copy inside each step, alone
+    finally:
         blk.close()
-        del x, x0, ws, mod
-        torch.cuda.empty_cache()
-    return out
+    tflops = shape.flops / (ms / 1e3) / 1e12
+    log(f"[bench] secondary {name} (key ranges {splits}): {ms:.3f} ms/step ({tflops:.0f} TFLOP/s) incl. setup "
+        f"{time.perf_counter() - t0:.1f}s")
+    return {
+        "n_tokens": shape.n_tokens, "d": shape.d, "dtype": shape.dtype,
+        "attn_chunk_tokens": ca, "mlp_chunk_tokens": cm, "ffn_chunk_features": fc,
+        **({"attention_splits": splits} if splits != 1 else {}),
+        "steps": steps, "ms_per_step": round(ms, 3), "copy_ms_per_step": round(copy_ms, 3),
+        "tokens_per_s": round(shape.n_tokens / (ms / 1e3), 1),
+        "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "peak_workspace_bytes": ws_bytes,
+    }
 
 
 def main() -> int:
