@@ -327,6 +327,24 @@ def test_attention_moving_maxima():
         assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
 
 
+def test_attention_split_with_moving_maxima():
+    # key ranges whose maxima differ by hundreds of units (growing key scales):
+    # the merge weights exp2((m_p - m) c) span a wide range; the result meets
+    # the bar and is the same bits in any query slice
+    n_q, n_kv, heads, dh = 300, 1000, 2, 128
+    q, k, v, tq, tk, tvt, tdt = _attn_inputs("bf16", n_q, n_kv, heads, dh, 23, scale=3.0, key_growth=0.5)
+    assert (_moves_after_first_tile(q, k, heads, dh) > 0).mean() > 0.9
+    full = torch.empty(n_q, heads * dh, dtype=tdt, device=DEV)
+    B.attention_split(tq, tk, tvt, full, heads, 3, n_kv=n_kv)
+    ref = O.attention(q, k, v, heads)
+    assert rel_l2(to_f64(full), ref) <= 1e-2
+    for a, b in ((0, 1), (33, 97), (255, 300)):
+        part = torch.empty(b - a, heads * dh, dtype=tdt, device=DEV)
+        B.attention_split(tq[a:b], tk, tvt, part, heads, 3, n_kv=n_kv)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu().view(torch.int16), full[a:b].cpu().view(torch.int16)), (a, b)
+
+
 def test_attention_overflowing_logits():
     # one key tile whose logits exceed the first tile's max by hundreds of
     # log2 units: its exponentials overflow fp32 (inf), which must move the
