@@ -331,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(const T* __restrict_
 
 // Largest tile sum of P before a query's running max moves (2^64). Every P
 // element then stays below 2^64, the row sum below 2^64 per 64-key tile
-// (2^80 at 2^16 tiles, a million keys) and |O| below that times max|V|, so
+// (2^80 at 2^16 tiles, four million keys) and |O| below that times max|V|, so
 // fp32 (to 2^128) and bf16 P (same exponent range) hold them with room for
 // |V| up to 2^40. A high bar keeps moves rare when logits are large (weights
 // of the int8 block give logits of tens to hundreds), where every move costs
