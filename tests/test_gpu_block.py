@@ -137,6 +137,63 @@ def test_closed_forms_on_device():
     check_bf16_bar(y1, O.block_forward(x, mod, w, one.n_heads))
 
 
+def test_permutation_equivariance(case):
+    # no positions and no mask: permuting the tokens permutes the output. The
+    # GPU path then sums each query's keys in another order, so the permuted
+    # run meets the bar against the permuted oracle output and against the
+    # permuted output of the unpermuted run, not bitwise
+    shape, inputs, x, y_ref = case
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(shape.n_tokens)
+    pin = dict(inputs)
+    pin["x"] = inputs["x"][perm].copy()
+    y = to_f64(run_block(shape, inputs, 256, 256))[perm]
+    yp = to_f64(run_block(shape, pin, 256, 256))
+    for ref in (y_ref[perm], y):
+        if shape.dtype == "f32":
+            assert max_abs(yp, ref) <= 1e-4 and rel_l2(yp, ref) <= 1e-4
+        else:
+            check_bf16_bar(yp, ref)
+
+
+def test_scale_minus_one_makes_every_token_attend_to_one_value(case):
+    # scale1 = -1: every normalised row becomes shift1, so all q, k and v rows
+    # are equal and each token's attention output is v itself
+    shape, inputs, x, _ = case
+    m = dict(inputs)
+    m["mod"] = inputs["mod"].copy()
+    m["mod"][1] = -1.0
+    xo, mod, w = oracle_inputs(m)
+    y_ref = O.block_forward(xo, mod, w, shape.n_heads)
+    y = to_f64(run_block(shape, m, 256, 256))
+    if shape.dtype == "f32":
+        assert max_abs(y, y_ref) <= 1e-4 and rel_l2(y, y_ref) <= 1e-4
+    else:
+        check_bf16_bar(y, y_ref)
+
+
+def test_zero_gate_weights_match_zero_mlp_gate_bitwise(case):
+    # W_g = 0 makes h = silu(0) * up = 0, so the MLP adds exactly zero to the
+    # fp32 stage and the output is the rounded stage, the same bytes as with
+    # gate2 = 0 (which multiplies the MLP branch by zero)
+    shape, inputs, x, _ = case
+    f = shape.ffn
+    wg = dict(inputs)
+    wg["w_gu"] = inputs["w_gu"].copy()
+    wg["w_gu"][:f] = 0
+    g2 = dict(inputs)
+    g2["mod"] = inputs["mod"].copy()
+    g2["mod"][5] = 0.0
+    a = run_block(shape, wg, 256, 256)
+    b = run_block(shape, g2, 256, 256)
+    assert bits(a) == bits(b)
+    xo, mod, w = oracle_inputs(g2)
+    y_ref = O.block_forward(xo, mod, w, shape.n_heads)  # x1, the residual after attention
+    if shape.dtype == "f32":
+        assert max_abs(to_f64(a), y_ref) <= 1e-4
+    else:
+        check_bf16_bar(to_f64(a), y_ref)
+
+
 def test_planned_chunks_run_within_budget():
     shape = SMALL["bf16"]
     inputs = synth.make_inputs(shape, 0)

@@ -393,6 +393,36 @@ def test_attention_split_matches_oracle(dtype, heads, dh, n_q, n_kv, splits):
     assert torch.equal(one.cpu(), plain.cpu())  # one range is the unsplit kernel
 
 
+@pytest.mark.parametrize("dh,n_q,n_kv,splits", [(128, 300, 1000, 1), (64, 257, 333, 1), (128, 70, 700, 3),
+                                                 (64, 33, 130, 2), (128, 1, 1, 1)])
+def test_attention_identical_keys_return_v_exactly(dh, n_q, n_kv, splits):
+    # Every key row equal and every value row equal: all of a query's scores
+    # are equal, so each P is exp2 of at most the rounding error of one score
+    # times the scale and rounds to exactly 1 in bf16; the row sum is the key
+    # count, and O = (count * v) / count = v, exact in fp32 (v has 8
+    # significant bits, the count at most 10). So the output holds v's bits
+    # for every query, also with a ragged last tile (its masked keys give P = 0)
+    # and with key ranges merged (every range has the same max, weight 1).
+    heads = 2
+    d = heads * dh
+    rng = _rng(n_q * 3 + n_kv + dh + splits)
+    q = bf16_round(rng.standard_normal((n_q, d)))
+    k1, v1 = (bf16_round(rng.standard_normal((1, d))) for _ in range(2))
+    k, v = np.repeat(k1, n_kv, axis=0), np.repeat(v1, n_kv, axis=0)
+    ld_vt = (n_kv + 63) // 64 * 64
+    vt = torch.zeros(d, ld_vt, dtype=torch.bfloat16, device=DEV)
+    vt[:, :n_kv] = _bf16(v).T
+    out = torch.empty(n_q, d, dtype=torch.bfloat16, device=DEV)
+    if splits == 1:
+        B.attention(_bf16(q), _bf16(k), vt, out, heads, n_kv=n_kv)
+    else:
+        B.attention_split(_bf16(q), _bf16(k), vt, out, heads, splits, n_kv=n_kv)
+    torch.cuda.synchronize()
+    want = np.repeat(v1, n_q, axis=0)
+    assert torch.equal(out.cpu(), _bf16(want).cpu())
+    assert max_abs(O.attention(q, k, v, heads), want) <= 1e-12  # the textbook result
+
+
 @pytest.mark.parametrize("scale", [1.0, 3.0])
 def test_attention_split_query_slices_bit_identical(scale):
     # with the key cut fixed by n_kv and the range count, a query's bits do not
