@@ -57,6 +57,26 @@ def test_bit_identical_across_chunks(case):
         assert bits(run_block(shape, inputs, ca, cm)) == ref, (ca, cm)
 
 
+@pytest.mark.parametrize("key", sorted(SMALL))
+@pytest.mark.parametrize("n", [2, 63, 65, 129])
+def test_small_token_counts(key, n):
+    # fewer tokens than one 64-key tile, one past it and one past two: every
+    # tile ragged, against the oracle and bit-identical across chunkings down
+    # to one-token slabs
+    shape = SMALL[key].replace(n_tokens=n)
+    inputs = synth.make_inputs(shape, seed=n)
+    x, mod, w = oracle_inputs(inputs)
+    y_ref = O.block_forward(x, mod, w, shape.n_heads)
+    y0 = run_block(shape, inputs, 0, n)
+    y = to_f64(y0)
+    if shape.dtype == "f32":
+        assert max_abs(y, y_ref) <= 1e-4 and rel_l2(y, y_ref) <= 1e-4
+    else:
+        check_bf16_bar(y, y_ref)
+    for ca, cm in ((1, 1), (n - 1, 2), (7, 5)):
+        assert bits(run_block(shape, inputs, ca, cm)) == bits(y0), (ca, cm)
+
+
 def test_deterministic_and_poisoned_workspace(case):
     shape, inputs, _, _ = case
     a = bits(run_block(shape, inputs, 128, 192))
