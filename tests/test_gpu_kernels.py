@@ -137,6 +137,37 @@ def test_linear_tile_shape_does_not_change_bits(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
+@pytest.mark.parametrize("m,n,k", [(300, 384, 512), (70, 512, 128), (16384, 1024, 512)])
+def test_linear_selection_weights_exact(dtype, m, n, k):
+    # Row j of W holds a single 0.5, at input column sel[j] (int8: q = 1 with
+    # row scale 0.5). Each output is then one exact product plus exact zeros,
+    # whatever the k order, so it must equal 0.5 * a[:, sel] bit for bit, in
+    # the 64-, 128- and 256-wide tiles alike. A transposed or misplaced operand
+    # fragment, a wrong k offset or a wrong row scale shows at once.
+    rng = _rng(m + 3 * n + k)
+    sel = rng.permutation(k)[:n] if n <= k else rng.integers(0, k, n)
+    a = rng.standard_normal((m, k))
+    a = a.astype(np.float32).astype(np.float64) if dtype == "f32" else bf16_round(a)
+    wf = np.zeros((n, k))
+    wf[np.arange(n), sel] = 0.5
+    want = 0.5 * a[:, sel]
+    if dtype == "f32":
+        ta, tw = (torch.from_numpy(t.astype(np.float32)).to(DEV) for t in (a, wf))
+        ts, expect = None, torch.from_numpy(want.astype(np.float32))
+    elif dtype == "bf16":
+        ta, tw, ts, expect = _bf16(a), _bf16(wf), None, _bf16(want).cpu()
+    else:
+        q = (wf != 0).astype(np.int8)
+        ta, tw = _bf16(a), torch.from_numpy(q).to(DEV)
+        ts = torch.full((n,), 0.5, dtype=torch.float32, device=DEV)
+        expect = _bf16(want).cpu()
+    out = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "store", ta, tw, out, n, w_scale=ts)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), expect)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
 def test_linear_store_transposed(dtype):
     m, n, k, ld = 203, 128, 256, 256
     a, wf, ta, tw, ts = _linear_case(dtype, m, n, k, 11)
