@@ -163,8 +163,15 @@ def test_linear_selection_weights_exact(dtype, m, n, k):
         expect = _bf16(want).cpu()
     out = torch.empty(m, n, dtype=_act_dtype(dtype), device=DEV)
     B.linear(dtype, "store", ta, tw, out, n, w_scale=ts)
+    # the transposed store (V^T of the K|V pass): the same values, columns
+    # past the last token untouched
+    ld = (m + 63) // 64 * 64
+    out_t = torch.zeros(n, ld, dtype=_act_dtype(dtype), device=DEV)
+    B.linear(dtype, "store_t", ta, tw, out_t, n, w_scale=ts)
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), expect)
+    assert torch.equal(out_t[:, :m].cpu(), expect.T.contiguous())
+    assert not out_t[:, m:].cpu().any()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "w8_bf16"])
