@@ -461,6 +461,34 @@ def test_attention_identical_keys_return_v_exactly(dh, n_q, n_kv, splits):
     assert max_abs(O.attention(q, k, v, heads), want) <= 1e-12  # the textbook result
 
 
+@pytest.mark.parametrize("dh,n_q,n_kv,splits", [(64, 300, 1000, 1), (128, 70, 200, 1), (64, 33, 130, 3)])
+def test_attention_identical_keys_return_v_f32(dh, n_q, n_kv, splits):
+    # The same closed form through the fp32 kernel. Its P is exp2 of at most
+    # the rounding error of one score times the scale, so 1 to within a few
+    # units of 2^-24, but v has 24 significant bits and the n_kv products p*v
+    # and the n_kv terms of the row sum are rounded as they accumulate: O is v
+    # to within 2 * n_kv * 2^-24 relative. A row sum off by one key, or a
+    # masked key counted, would miss by 1/n_kv, far above that.
+    heads = 2
+    d = heads * dh
+    rng = _rng(n_q * 5 + n_kv + dh + splits)
+    q = rng.standard_normal((n_q, d)).astype(np.float32).astype(np.float64)
+    k1, v1 = (rng.standard_normal((1, d)).astype(np.float32).astype(np.float64) for _ in range(2))
+    k, v = np.repeat(k1, n_kv, axis=0), np.repeat(v1, n_kv, axis=0)
+    ld_vt = (n_kv + 63) // 64 * 64
+    vt = torch.zeros(d, ld_vt, dtype=torch.float32, device=DEV)
+    vt[:, :n_kv] = torch.from_numpy(v.astype(np.float32)).to(DEV).T
+    tq, tk = (torch.from_numpy(t.astype(np.float32)).to(DEV) for t in (q, k))
+    out = torch.empty(n_q, d, dtype=torch.float32, device=DEV)
+    if splits == 1:
+        B.attention(tq, tk, vt, out, heads, n_kv=n_kv)
+    else:
+        B.attention_split(tq, tk, vt, out, heads, splits, n_kv=n_kv)
+    got = to_f64(out)
+    want = np.repeat(v1, n_q, axis=0)
+    assert np.all(np.abs(got - want) <= 2.0 * n_kv * 2.0 ** -24 * np.abs(want) + 1e-30)
+
+
 @pytest.mark.parametrize("scale", [1.0, 3.0])
 def test_attention_split_query_slices_bit_identical(scale):
     # with the key cut fixed by n_kv and the range count, a query's bits do not
