@@ -438,17 +438,20 @@ def secondary_configs(steps: int) -> dict:
     settings (one warm-up, `steps` timed forwards each, HIP events on the
     library's stream), so that one default run records them beside the large
     block: the mid block (also with two key ranges per query, its measured
-    best), the long clip with FFN feature slices and the int8-weight block."""
+    best, and unchunked, as its workload also defines), the long clip with
+    FFN feature slices and the int8-weight block."""
     import torch
 
     from memory_bounded_chunked_amd import block as B
     from memory_bounded_chunked_amd import synth
     dev = "cuda:0"
     out = {}
-    for name, splits in (("mid", 1), ("mid", 2), ("longclip", 1), ("int8", 1)):
+    for name, splits, unchunked in (("mid", 1, False), ("mid", 2, False), ("mid", 1, True), ("longclip", 1, False),
+                                    ("int8", 1, False)):
         key = name if splits == 1 else f"{name}_splits{splits}"
+        key += "_unchunked" if unchunked else ""
         try:
-            out[key] = _time_secondary(B, synth, dev, name, splits, steps)
+            out[key] = _time_secondary(B, synth, dev, name, splits, steps, unchunked)
         except Exception as e:  # reported in the record; the headline line still prints
             out[key] = {"error": f"{type(e).__name__}: {e}"}
             log(f"[bench] secondary {key} failed: {e}")
@@ -456,8 +459,9 @@ def secondary_configs(steps: int) -> dict:
     return out
 
 
-def _time_secondary(B, synth, dev, name, splits, steps) -> dict:
-    """One configuration of secondary_configs: its record."""
+def _time_secondary(B, synth, dev, name, splits, steps, unchunked=False) -> dict:
+    """One configuration of secondary_configs: its record (unchunked: one
+    attention slice of all tokens and one MLP slab, the stock schedule)."""
     import torch
     shape = synth.CONFIGS[name]
     t0 = time.perf_counter()
@@ -468,6 +472,8 @@ def _time_secondary(B, synth, dev, name, splits, steps) -> dict:
         if splits != 1:
             blk.set_attention_splits(splits)
         ca, cm, fc = shape.attn_chunk, shape.mlp_chunk, shape.ffn_chunk
+        if unchunked:
+            ca, cm = 0, shape.n_tokens
         ws_bytes = blk.peak_workspace(shape.n_tokens, ca, cm, fc)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         x = x0.clone()
@@ -493,7 +499,8 @@ def _time_secondary(B, synth, dev, name, splits, steps) -> dict:
     finally:
         blk.close()
     tflops = shape.flops / (ms / 1e3) / 1e12
-    log(f"[bench] secondary {name} (key ranges {splits}): {ms:.3f} ms/step ({tflops:.0f} TFLOP/s) incl. setup "
+    log(f"[bench] secondary {name} (chunks {ca}/{cm}, key ranges {splits}): {ms:.3f} ms/step ({tflops:.0f} TFLOP/s) "
+        f"incl. setup "
         f"{time.perf_counter() - t0:.1f}s")
     return {
         "n_tokens": shape.n_tokens, "d": shape.d, "dtype": shape.dtype,
