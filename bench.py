@@ -435,7 +435,7 @@ def copy_roofline(config: str) -> int:
 
 def secondary_configs(steps: int) -> dict:
     """Short timing of the other block configurations at their own chunk
-    settings (one warm-up, `steps` timed forwards each, HIP events on the
+    settings (two warm-ups, `steps` timed forwards each, HIP events on the
     library's stream), so that one default run records them beside the large
     block: the mid block (also with two key ranges per query, its measured
     best, and unchunked, as its workload also defines), the long clip with
@@ -492,7 +492,8 @@ def _time_secondary(B, synth, dev, name, splits, steps, unchunked=False) -> dict
             torch.cuda.synchronize()
             return ev0.elapsed_time(ev1) / steps
 
-        step()
+        for _ in range(2):
+            step()
         torch.cuda.synchronize()
         ms = timed(step)
         copy_ms = timed(lambda: x.copy_(x0))  # the restoring copy inside each step, alone
@@ -542,7 +543,7 @@ def main() -> int:
                     help="write the traffic record of KERNEL from two counter_collection.csv files")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the short timing of the other configurations that the default run adds")
-    ap.add_argument("--secondary-steps", type=int, default=3)
+    ap.add_argument("--secondary-steps", type=int, default=5)
     args = ap.parse_args()
     if args.record_traffic:
         return record_traffic(*args.record_traffic)
